@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of one rank's tensor-parallel MLP shard on one MI355X.
+
+Workload: the Llama-3-70B FFN shard (N = 4096 tokens, D = 8192, F = 28672 split T = 8 ways,
+F/T = 3584; shard 0), bf16 inputs, fp32 accumulation, GELU (tanh form). One step is the
+forward shard through the C ABI: the column-parallel up-projection with fused bias + GELU
+(mlp_tp_up_proj) and the row-parallel down-projection to the fp32 partial (mlp_tp_down_proj).
+`value` is the forward's GEMM work (4 N D F/T flops) per second.
+
+Also measured in the same run, each over its own timed loop (reported under "rows"): the
+block-tail reduction of 8 fp32 partials [2048, 12288] with b2 (the GPT-3-175B layer's tail),
+the shard backward at the Llama shape, and the sum of 8 dX partials [4096, 8192].
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "TP-shard MLP fwd TFLOP/s + % bf16 MFMA peak (D=8192, F/T=3584, N=4096)"
+KERNEL_SOURCES = ("gemm_mfma.hpp", "epilogue.hpp", "dispatch.hpp", "fwd.hip", "common.hpp",
+                  "reduce.hip", "bwd.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tensor_mlp_block_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources (its recorded source hash matches); else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="skip the extra per-row timings")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the shard runs on one GPU; see the design notes for how it would shard).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from tensor_mlp_block_amd import binding as mt
+    from tensor_mlp_block_amd import synth, workloads
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    mt.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = workloads.LLAMA70B_SHARD_T8
+    N, D, F, T, Fs = w.N, w.D, w.F, w.T, w.Fs
+    log(f"[bench] workload {w.name}: generating inputs")
+    Xc = synth.gen_X(w)
+    W1c, b1c, W2c = synth.gen_W1(w, 0, Fs), synth.gen_b1(w, 0, Fs), synth.gen_W2(w, 0, Fs)
+    X, W1, b1, W2 = Xc.to(dev), W1c.to(dev), b1c.to(dev), W2c.to(dev)
+    H = torch.empty((N, Fs), dtype=torch.bfloat16, device=dev)
+    P = torch.empty((N, D), dtype=torch.float32, device=dev)
+
+    def step():
+        mt.mlp_tp_up_proj(X, W1, b1, None, H, N, D, F, T, mt.BF16, w.act)
+        mt.mlp_tp_down_proj(H, W2, P, N, D, F, T, mt.BF16)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, HIP events between the two launches of every step (all on
+    # torch's current stream, which is the stream the binding launches on).
+    K = args.steps
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        mt.mlp_tp_up_proj(X, W1, b1, None, H, N, D, F, T, mt.BF16, w.act)
+        ev[i][1].record(stream)
+        mt.mlp_tp_down_proj(H, W2, P, N, D, F, T, mt.BF16)
+        ev[i][2].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    up_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    down_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    ms_per_step = total_ms / K
+    gemm_flop = 2.0 * N * D * Fs
+    fwd_flop = 2.0 * gemm_flop
+    value = fwd_flop / (ms_per_step * 1e-3) / 1e12
+    mean_up, mean_down = sum(up_ms) / K, sum(down_ms) / K
+    log(f"[bench] step {ms_per_step:.4f} ms  up {mean_up:.4f} ms  down {mean_down:.4f} ms  "
+        f"{value:.1f} TFLOP/s")
+
+    dominant = "up_proj" if mean_up >= mean_down else "down_proj"
+    dom_ms = max(mean_up, mean_down)
+    achieved = gemm_flop / (dom_ms * 1e-3) / 1e12
+    kernel_name = {"up_proj": "gemm_up_proj_bias_gelu", "down_proj": "gemm_down_proj_f32"}[dominant]
+    roofline = {
+        "kernel": kernel_name,
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": read_traffic(kernel_name, w.name),
+        "algorithmic_flop_per_launch": gemm_flop,
+        "mean_launch_ms": round(dom_ms, 5),
+        "other_kernel": {"name": ("gemm_down_proj_f32" if dominant == "up_proj"
+                                  else "gemm_up_proj_bias_gelu"),
+                         "mean_launch_ms": round(min(mean_up, mean_down), 5),
+                         "achieved": round(gemm_flop / (min(mean_up, mean_down) * 1e-3) / 1e12, 2)},
+    }
+
+    rows = None
+    if not args.no_rows:
+        rows = measure_rows(torch, mt, synth, workloads, dev, X, W1, b1, W2, H, w)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(Xc, W1c, b1c, W2c, w, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": w.name, "N": N, "D": D, "F": F, "T": T, "Fs": Fs, "shard": 0,
+                   "act": w.act, "parallelism": "one rank's shard on 1 GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": rows,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _time_loop(torch, fn, iters, warm=3):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    s = torch.cuda.current_stream()
+    a.record(s)
+    for _ in range(iters):
+        fn()
+    b.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def measure_rows(torch, mt, synth, workloads, dev, X, W1, b1, W2, H, w):
+    res = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+
+    # Block tail of the GPT-3-175B layer: 8 fp32 partials [2048, 12288] + bf16 b2, once.
+    w4 = workloads.GPT3_175B_T8
+    parts = [torch.randn((w4.N, w4.D), generator=g, device=dev) for _ in range(w4.T)]
+    b2 = synth.gen_b2(w4).to(dev)
+    Y = torch.empty((w4.N, w4.D), device=dev)
+    ms = _time_loop(torch, lambda: mt.mlp_tp_partial_reduce(parts, w4.T, b2, mt.BF16, Y, w4.N,
+                                                            w4.D), 20)
+    nbytes = (w4.T + 1) * 4.0 * w4.N * w4.D + 2.0 * w4.D
+    res["partial_reduce"] = {"workload": w4.name, "T": w4.T, "ms": round(ms, 5),
+                             "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "algorithmic_bytes": nbytes}
+    log(f"[bench] reduce T=8 [2048,12288]: {ms:.4f} ms, {res['partial_reduce']['GB/s']} GB/s")
+    del parts, Y
+
+    # Backward of the Llama shard (dY ~ N(0,1), seed 505).
+    w5 = workloads.LLAMA70B_SHARD_T8_BWD
+    N, D, F, T, Fs = w5.N, w5.D, w5.F, w5.T, w5.Fs
+    dY = synth.gen_dY(w5).to(dev)
+    Z = torch.empty((N, Fs), dtype=torch.bfloat16, device=dev)
+    Hz = torch.empty((N, Fs), dtype=torch.bfloat16, device=dev)
+    P = torch.empty((N, D), device=dev)
+    mt.mlp_tp_shard_fwd(X, W1, b1, W2, Hz, Z, P, N, D, F, T, mt.BF16, w5.act)
+    dZ = torch.empty((N, Fs), dtype=torch.bfloat16, device=dev)
+    dW1 = torch.empty((D, Fs), device=dev)
+    dW2 = torch.empty((Fs, D), device=dev)
+    db1 = torch.empty((Fs,), device=dev)
+    dX = torch.empty((N, D), device=dev)
+    nb = mt.mlp_tp_shard_bwd_workspace_bytes(N, D, F, T)
+    ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
+    ms = _time_loop(torch, lambda: mt.mlp_tp_shard_bwd(X, W1, W2, Z, Hz, dY, dZ, dW1, db1, dW2,
+                                                       dX, ws, nb, N, D, F, T, mt.BF16,
+                                                       w5.act), 10)
+    flop = 8.0 * N * D * Fs
+    res["shard_bwd"] = {"workload": w5.name, "ms": round(ms, 5),
+                        "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1),
+                        "frac_mfma": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    log(f"[bench] shard bwd: {ms:.4f} ms, {res['shard_bwd']['TFLOP/s']} TFLOP/s")
+    del dZ, dW1, dW2, db1, Z, Hz, P
+
+    # Sum of the 8 dX partials [4096, 8192] (no bias).
+    parts = [torch.randn((N, D), generator=g, device=dev) for _ in range(T)]
+    ms = _time_loop(torch, lambda: mt.mlp_tp_partial_reduce(parts, T, None, mt.F32, dX, N, D), 20)
+    nbytes = (T + 1) * 4.0 * N * D
+    res["sum_dx"] = {"workload": w5.name, "T": T, "ms": round(ms, 5),
+                     "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": nbytes}
+    log(f"[bench] sum dX T=8 [4096,8192]: {ms:.4f} ms, {res['sum_dx']['GB/s']} GB/s")
+    del parts
+    return res
+
+
+def cpu_baseline(Xc, W1c, b1c, W2c, w, seconds):
+    """The fp64 oracle, as it stands, on a bounded sample of token rows of the same shard."""
+    import numpy as np
+    import oracle
+
+    W1, b1, W2 = (t.double().numpy() for t in (W1c, b1c, W2c))
+    X = Xc.double().numpy()
+    per_row_flop = 4.0 * w.D * w.Fs
+    t = time.perf_counter()
+    oracle.shard_fwd(X[:2], W1, b1, W2, 1, 0, act=w.act)
+    dt = (time.perf_counter() - t) / 2
+    rows = int(max(4, min(w.N, seconds / max(dt, 1e-6))))
+    idx = np.linspace(0, w.N - 1, rows).astype(np.int64)
+    log(f"[bench] cpu baseline: {rows} rows (~{rows * dt:.1f} s)")
+    t = time.perf_counter()
+    oracle.shard_fwd(X[idx], W1, b1, W2, 1, 0, act=w.act)
+    el = time.perf_counter() - t
+    tflops = rows * per_row_flop / el / 1e12
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(el, 2),
+            "sample": f"{rows} of {w.N} token rows of the {w.name} shard-0 forward "
+                      f"(fp64 C oracle, OpenMP over rows)"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,168 @@
+/*
+ * mlp_tp.h -- C ABI of libmlptp.so: one rank's tensor-parallel MLP shard on an MI355X (gfx950).
+ *
+ * Pages cited, as [tag section]:
+ *   [Z] zwjcode.cn, "一层 MLP 太宽而放不下时怎样切？列并行、行并行与块尾归约"
+ *   [C] charliedreemur.github.io, "TP:Column / Row Parallel Linear 怎么切? MLP 和 attention 怎么切?"
+ *   [U] unpurerationalist.github.io, "LLM Systems 16: Model Parallel Training"
+ *   [J] jwzheng96.github.io, "张量并行 TP 与列并行 / 行并行的实现" (Megatron-LM tutorial ch. 7)
+ *
+ * The method. An MLP H = phi(X W1 + b1), Y = H W2 + b2 [Z 01] is split over T ranks: W1 by
+ * columns and W2 by the matching rows [Z 02], [U 3.2], [J 7.2]. Rank r (Fs = F / T hidden
+ * columns) computes
+ *     Z^(r) = X W1^(r) + b1^(r),   H^(r) = phi(Z^(r)),   P^(r) = H^(r) W2^(r)
+ * with no exchange; P^(r) is a full-shape [N, D] partial. The block tail sums the partials
+ * and adds b2 exactly once: Y = sum_r P^(r) + b2 [Z 02], [Z 05], [U 3.8]. In the backward,
+ * each rank forms its own weight gradients locally; the input gradient is a sum of per-rank
+ * partials dX^(r) = dZ^(r) W1^(r)^T [Z 06], [U 3.6.1].
+ *
+ * Conventions shared by every entry point:
+ *   - Shapes are GLOBAL: callers pass the full FFN width F and the shard count T; the library
+ *     derives Fs = F / T itself and rejects F % T != 0 [U 3.8] ("local vs global shape": [Z 07]).
+ *   - N (tokens, the [B, L, D] activation flattened to [N, D] row-major [Z 04]) may be 0: the
+ *     call is then a no-op that returns MLP_TP_OK. D, F must be > 0 and T >= 1.
+ *   - All tensors are dense row-major with no padding. Pointers are DEVICE pointers (HIP
+ *     device memory of the current device) unless stated otherwise, each 16-byte aligned.
+ *   - dtype selects the element type of X, W1^(r), b1^(r), W2^(r), H, Z, dY and dZ:
+ *     MLP_TP_F32 (float) or MLP_TP_BF16 (bfloat16, stored as 16-bit words). Partials, Y and
+ *     every gradient except dZ are always float. Products accumulate in fp32; bf16 results
+ *     (H, Z, dZ) are rounded to nearest even once.
+ *   - Every call is asynchronous on the caller's HIP stream (a hipStream_t passed as void*;
+ *     NULL is the null stream). The library never allocates, frees or synchronises; the
+ *     caller owns all memory and must keep it alive until the stream has run the work.
+ *   - Every argument is validated on the host BEFORE any HIP call; a failed check returns its
+ *     negative code and launches nothing. MLP_TP_E_HIP reports a launch failure seen by
+ *     hipGetLastError after the launches (the stream may then hold part of the work).
+ *   - Outputs must not overlap inputs or each other (MLP_TP_E_ALIAS), except where stated.
+ */
+#ifndef MLP_TP_H
+#define MLP_TP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MLP_TP_OK 0
+#define MLP_TP_E_NULL (-1)        /* a required pointer is NULL */
+#define MLP_TP_E_SHAPE (-2)       /* N < 0, D <= 0, F <= 0, T < 1, or T above the limit */
+#define MLP_TP_E_INDIVISIBLE (-3) /* F % T != 0 */
+#define MLP_TP_E_DTYPE (-4)       /* unknown dtype code */
+#define MLP_TP_E_ACT (-5)         /* unknown activation code */
+#define MLP_TP_E_ALIGN (-6)       /* a pointer is not 16-byte aligned */
+#define MLP_TP_E_WORKSPACE (-7)   /* workspace NULL or smaller than the query returns */
+#define MLP_TP_E_HIP (-8)         /* a HIP launch failed */
+#define MLP_TP_E_ALIAS (-9)       /* an output overlaps an input or another output */
+
+/* Element types. */
+#define MLP_TP_F32 0
+#define MLP_TP_BF16 1
+
+/* Activations phi. GELU_TANH is 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))); GELU_ERF is
+   z Phi(z); GELU_SIGMOID is z / (1 + exp(-1.702 z)) (the form in [C 代码]); RELU'(0) = 0. */
+#define MLP_TP_ACT_IDENTITY 0
+#define MLP_TP_ACT_RELU 1
+#define MLP_TP_ACT_GELU_TANH 2
+#define MLP_TP_ACT_GELU_ERF 3
+#define MLP_TP_ACT_GELU_SIGMOID 4
+
+/* Largest shard count mlp_tp_partial_reduce accepts in one call. */
+#define MLP_TP_MAX_REDUCE_T 64
+
+/*
+ * Column-parallel up-projection with fused bias and activation [Z 02], [Z 05], [U 3.8]:
+ *     Z = X . W1r + b1r   (fp32 accumulate),   H = phi(Z).
+ *   X   [N, D]   dtype, replicated input.
+ *   W1r [D, Fs]  dtype, this rank's column slice W1[:, r*Fs:(r+1)*Fs], itself row-major.
+ *   b1r [Fs]     dtype, the matching slice of b1; NULL means no bias.
+ *   Z   [N, Fs]  dtype output, pre-activation kept for the backward; NULL skips it.
+ *   H   [N, Fs]  dtype output, the activation.
+ * Errors: E_NULL (X, W1r, H), E_SHAPE, E_INDIVISIBLE, E_DTYPE, E_ACT, E_ALIGN, E_ALIAS
+ * (H or Z overlapping X, W1r, b1r or each other), E_HIP.
+ */
+int mlp_tp_up_proj(const void* X, const void* W1r, const void* b1r, void* Z, void* H,
+                   int64_t N, int64_t D, int64_t F, int32_t T, int32_t dtype, int32_t act,
+                   void* stream);
+
+/*
+ * Row-parallel down-projection to this rank's full-shape partial [Z 02], [J 7.2]:
+ *     P = H . W2r   (fp32 accumulate and output, NO b2: b2 belongs to the block tail [Z 05]).
+ *   H   [N, Fs]  dtype.   W2r [Fs, D] dtype, the row slice W2[r*Fs:(r+1)*Fs, :].
+ *   P   [N, D]   float output.
+ * Errors: E_NULL, E_SHAPE, E_INDIVISIBLE, E_DTYPE, E_ALIGN, E_ALIAS (P overlapping H or W2r),
+ * E_HIP.
+ */
+int mlp_tp_down_proj(const void* H, const void* W2r, float* P, int64_t N, int64_t D, int64_t F,
+                     int32_t T, int32_t dtype, void* stream);
+
+/*
+ * One rank's forward shard: mlp_tp_up_proj then mlp_tp_down_proj on the same stream [Z 02].
+ * There is deliberately no b2 argument: adding b2 per rank would give Y + T b2 after the
+ * sum [Z 05]; b2 is taken only by mlp_tp_partial_reduce.
+ *   X [N, D], W1r [D, Fs], b1r [Fs] (nullable), W2r [Fs, D]: dtype inputs.
+ *   H [N, Fs] dtype output; Z [N, Fs] dtype output (nullable, needed for the backward);
+ *   P [N, D] float output.
+ * Errors: those of the two calls; all arguments are checked before the first launch.
+ */
+int mlp_tp_shard_fwd(const void* X, const void* W1r, const void* b1r, const void* W2r, void* H,
+                     void* Z, float* P, int64_t N, int64_t D, int64_t F, int32_t T,
+                     int32_t dtype, int32_t act, void* stream);
+
+/*
+ * Block-tail reduction on one GPU [Z 02], [Z 04], [Z 05], [U 3.8]:
+ *     Y = (((P[0] + P[1]) + ...) + P[T-1]) + b2     (fp32, shards summed in rank order,
+ *                                                    b2 added exactly once, last).
+ * This is the sum the all-reduce of the row-parallel output performs, over T partial buffers
+ * resident in this GPU's memory. With b2 = NULL it is the plain sum, e.g. of the input-gradient
+ * partials dX^(r) [Z 06].
+ *   P   HOST array of T device pointers, each to a float [N, D] partial.
+ *   T   1 <= T <= MLP_TP_MAX_REDUCE_T.
+ *   b2  [D] of b2_dtype (MLP_TP_F32 or MLP_TP_BF16); NULL means no bias.
+ *   Y   [N, D] float output. Y may be exactly equal to any P[r] (in-place); a partial overlap
+ *       with any P[r] or with b2 is E_ALIAS.
+ * Errors: E_NULL (P, any P[r], Y), E_SHAPE (N < 0, D <= 0, T outside the range), E_DTYPE,
+ * E_ALIGN, E_ALIAS, E_HIP.
+ */
+int mlp_tp_partial_reduce(const float* const* P, int32_t T, const void* b2, int32_t b2_dtype,
+                          float* Y, int64_t N, int64_t D, void* stream);
+
+/*
+ * Bytes of device workspace mlp_tp_shard_bwd needs for these sizes (0 if none); a negative
+ * MLP_TP_E_* code for invalid sizes.
+ */
+int64_t mlp_tp_shard_bwd_workspace_bytes(int64_t N, int64_t D, int64_t F, int32_t T);
+
+/*
+ * Backward of one rank's shard for the upstream gradient dY of the block output [Z 06],
+ * [U 3.6.1], [C 推导 / 关键公式]:
+ *     dH   = dY . W2r^T                 (no exchange: the row-parallel backward is local)
+ *     dZ   = dH (.) phi'(Z)             (through the local activation)
+ *     dW2r = H^T . dY      dW1r = X^T . dZ      db1r = sum over tokens of dZ
+ *     dXr  = dZ . W1r^T                 (this rank's partial of dX; the sum over ranks,
+ *                                        e.g. by mlp_tp_partial_reduce with b2 = NULL, is dX)
+ *   Inputs (dtype): X [N, D], W1r [D, Fs], W2r [Fs, D], Z [N, Fs] and H [N, Fs] as saved by the
+ *   forward, dY [N, D].
+ *   Outputs: dZ [N, Fs] dtype; dW1r [D, Fs], db1r [Fs] (nullable), dW2r [Fs, D] and
+ *   dXr [N, D], all float.
+ *   workspace: device scratch of at least mlp_tp_shard_bwd_workspace_bytes(N, D, F, T)
+ *   bytes (ignored when that is 0), owned by the caller, contents not preserved.
+ * Errors: E_NULL, E_SHAPE, E_INDIVISIBLE, E_DTYPE, E_ACT, E_ALIGN, E_WORKSPACE, E_ALIAS
+ * (any output overlapping an input, another output or the workspace), E_HIP.
+ */
+int mlp_tp_shard_bwd(const void* X, const void* W1r, const void* W2r, const void* Z,
+                     const void* H, const void* dY, void* dZ, float* dW1r, float* db1r,
+                     float* dW2r, float* dXr, void* workspace, size_t workspace_bytes,
+                     int64_t N, int64_t D, int64_t F, int32_t T, int32_t dtype, int32_t act,
+                     void* stream);
+
+/* Static description of a return code; never NULL. */
+const char* mlp_tp_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLP_TP_H */

@@ -1,0 +1,245 @@
+// api.hip -- the extern "C" entry points of libmlptp.so (declared in include/mlp_tp.h).
+//
+// Each entry point validates every argument on the host before any HIP call, derives the
+// shard width Fs = F / T from the global sizes, then enqueues its kernels on the caller's
+// stream. Nothing here allocates, frees or synchronises.
+//
+// Pages cited, as [tag section]:
+//   [Z] zwjcode.cn, "一层 MLP 太宽而放不下时怎样切？列并行、行并行与块尾归约"
+//   [U] unpurerationalist.github.io, "LLM Systems 16: Model Parallel Training"
+#include "../../include/mlp_tp.h"
+#include "launch.hpp"
+
+#include <stdint.h>
+
+namespace {
+
+using mlptp::kBF16;
+using mlptp::kF32;
+
+// Sizes above this are rejected so byte counts and grid sizes cannot overflow.
+constexpr int64_t kMaxDim = INT32_MAX;
+constexpr int64_t kMaxElems = int64_t(1) << 56;
+
+struct Span {
+    const void* p;
+    int64_t bytes;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(Span a, Span b)
+{
+    if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
+}
+
+int elem_size(int32_t dtype) { return dtype == MLP_TP_BF16 ? 2 : 4; }
+
+bool dtype_ok(int32_t dtype) { return dtype == MLP_TP_F32 || dtype == MLP_TP_BF16; }
+
+bool act_ok(int32_t act) { return act >= MLP_TP_ACT_IDENTITY && act <= MLP_TP_ACT_GELU_SIGMOID; }
+
+// Shape rules shared by the shard calls: N >= 0, D > 0, F > 0, T >= 1, T | F [U 3.8].
+int check_shard_shape(int64_t N, int64_t D, int64_t F, int32_t T)
+{
+    if (N < 0 || D <= 0 || F <= 0 || T < 1) return MLP_TP_E_SHAPE;
+    if (N > kMaxDim || D > kMaxDim || F > kMaxDim) return MLP_TP_E_SHAPE;
+    if (F % T != 0) return MLP_TP_E_INDIVISIBLE;
+    const int64_t Fs = F / T;
+    if (N * Fs > kMaxElems || N * D > kMaxElems || D * Fs > kMaxElems) return MLP_TP_E_SHAPE;
+    // Grid sizes: one workgroup per 64 x 64 tile or larger, for every product of the shard.
+    const int64_t tn = (N + 63) / 64, td = (D + 63) / 64, tf = (Fs + 63) / 64;
+    if (tn * td > INT32_MAX || tn * tf > INT32_MAX || td * tf > INT32_MAX) return MLP_TP_E_SHAPE;
+    return MLP_TP_OK;
+}
+
+int all_aligned(std::initializer_list<const void*> ps)
+{
+    for (const void* p : ps)
+        if (p && !aligned16(p)) return MLP_TP_E_ALIGN;
+    return MLP_TP_OK;
+}
+
+// Every span in `outs` must be disjoint from every span in `ins` and from the other outs.
+int disjoint(std::initializer_list<Span> outs, std::initializer_list<Span> ins)
+{
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (const Span& i : ins)
+            if (overlap(*o, i)) return MLP_TP_E_ALIAS;
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlap(*o, *o2)) return MLP_TP_E_ALIAS;
+    }
+    return MLP_TP_OK;
+}
+
+int launch_status()
+{
+    return hipGetLastError() == hipSuccess ? MLP_TP_OK : MLP_TP_E_HIP;
+}
+
+int check_up(const void* X, const void* W1r, const void* b1r, void* Z, void* H, int64_t N,
+             int64_t D, int64_t F, int32_t T, int32_t dtype, int32_t act)
+{
+    if (!X || !W1r || !H) return MLP_TP_E_NULL;
+    if (int rc = check_shard_shape(N, D, F, T)) return rc;
+    if (!dtype_ok(dtype)) return MLP_TP_E_DTYPE;
+    if (!act_ok(act)) return MLP_TP_E_ACT;
+    if (int rc = all_aligned({X, W1r, b1r, Z, H})) return rc;
+    const int64_t es = elem_size(dtype), Fs = F / T;
+    return disjoint({{H, N * Fs * es}, {Z, N * Fs * es}},
+                    {{X, N * D * es}, {W1r, D * Fs * es}, {b1r, Fs * es}});
+}
+
+int check_down(const void* H, const void* W2r, const float* P, int64_t N, int64_t D, int64_t F,
+               int32_t T, int32_t dtype)
+{
+    if (!H || !W2r || !P) return MLP_TP_E_NULL;
+    if (int rc = check_shard_shape(N, D, F, T)) return rc;
+    if (!dtype_ok(dtype)) return MLP_TP_E_DTYPE;
+    if (int rc = all_aligned({H, W2r, P})) return rc;
+    const int64_t es = elem_size(dtype), Fs = F / T;
+    return disjoint({{P, N * D * 4}}, {{H, N * Fs * es}, {W2r, Fs * D * es}});
+}
+
+}  // namespace
+
+extern "C" {
+
+int mlp_tp_up_proj(const void* X, const void* W1r, const void* b1r, void* Z, void* H, int64_t N,
+                   int64_t D, int64_t F, int32_t T, int32_t dtype, int32_t act, void* stream)
+{
+    if (int rc = check_up(X, W1r, b1r, Z, H, N, D, F, T, dtype, act)) return rc;
+    if (N == 0) return MLP_TP_OK;
+    mlptp::launch_up_proj(X, W1r, b1r, Z, H, N, D, F / T, dtype, act,
+                          static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int mlp_tp_down_proj(const void* H, const void* W2r, float* P, int64_t N, int64_t D, int64_t F,
+                     int32_t T, int32_t dtype, void* stream)
+{
+    if (int rc = check_down(H, W2r, P, N, D, F, T, dtype)) return rc;
+    if (N == 0) return MLP_TP_OK;
+    mlptp::launch_down_proj(H, W2r, P, N, D, F / T, dtype, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int mlp_tp_shard_fwd(const void* X, const void* W1r, const void* b1r, const void* W2r, void* H,
+                     void* Z, float* P, int64_t N, int64_t D, int64_t F, int32_t T,
+                     int32_t dtype, int32_t act, void* stream)
+{
+    if (int rc = check_up(X, W1r, b1r, Z, H, N, D, F, T, dtype, act)) return rc;
+    if (int rc = check_down(H, W2r, P, N, D, F, T, dtype)) return rc;
+    {
+        const int64_t es = elem_size(dtype), Fs = F / T;
+        // P is written after H is complete; it must still not clobber any input or Z.
+        if (int rc = disjoint({{P, N * D * 4}}, {{X, N * D * es}, {W1r, D * Fs * es},
+                                                  {b1r, Fs * es}, {Z, N * Fs * es}}))
+            return rc;
+        if (int rc = disjoint({{H, N * Fs * es}, {Z, N * Fs * es}}, {{W2r, Fs * D * es}}))
+            return rc;
+    }
+    if (N == 0) return MLP_TP_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    mlptp::launch_up_proj(X, W1r, b1r, Z, H, N, D, F / T, dtype, act, s);
+    if (int rc = launch_status()) return rc;
+    mlptp::launch_down_proj(H, W2r, P, N, D, F / T, dtype, s);
+    return launch_status();
+}
+
+int mlp_tp_partial_reduce(const float* const* P, int32_t T, const void* b2, int32_t b2_dtype,
+                          float* Y, int64_t N, int64_t D, void* stream)
+{
+    if (!P || !Y) return MLP_TP_E_NULL;
+    if (T < 1 || T > MLP_TP_MAX_REDUCE_T || N < 0 || D <= 0 || N > kMaxDim || D > kMaxDim ||
+        N * D > kMaxElems)
+        return MLP_TP_E_SHAPE;
+    for (int32_t r = 0; r < T; ++r)
+        if (!P[r]) return MLP_TP_E_NULL;
+    if (b2 && !dtype_ok(b2_dtype)) return MLP_TP_E_DTYPE;
+    if (!aligned16(Y) || (b2 && !aligned16(b2))) return MLP_TP_E_ALIGN;
+    for (int32_t r = 0; r < T; ++r)
+        if (!aligned16(P[r])) return MLP_TP_E_ALIGN;
+    const int64_t bytes = N * D * 4;
+    for (int32_t r = 0; r < T; ++r)
+        if (P[r] != Y && overlap({Y, bytes}, {P[r], bytes})) return MLP_TP_E_ALIAS;
+    if (b2 && overlap({Y, bytes}, {b2, D * elem_size(b2_dtype)})) return MLP_TP_E_ALIAS;
+    if (N == 0) return MLP_TP_OK;
+    mlptp::launch_partial_reduce(P, T, b2, b2_dtype, Y, N, D, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int64_t mlp_tp_shard_bwd_workspace_bytes(int64_t N, int64_t D, int64_t F, int32_t T)
+{
+    if (int rc = check_shard_shape(N, D, F, T)) return rc;
+    if (N == 0) return 0;
+    return mlptp::colsum_workspace_bytes(N, F / T);
+}
+
+int mlp_tp_shard_bwd(const void* X, const void* W1r, const void* W2r, const void* Z,
+                     const void* H, const void* dY, void* dZ, float* dW1r, float* db1r,
+                     float* dW2r, float* dXr, void* workspace, size_t workspace_bytes,
+                     int64_t N, int64_t D, int64_t F, int32_t T, int32_t dtype, int32_t act,
+                     void* stream)
+{
+    if (!X || !W1r || !W2r || !Z || !H || !dY || !dZ || !dW1r || !dW2r || !dXr)
+        return MLP_TP_E_NULL;
+    if (int rc = check_shard_shape(N, D, F, T)) return rc;
+    if (!dtype_ok(dtype)) return MLP_TP_E_DTYPE;
+    if (!act_ok(act)) return MLP_TP_E_ACT;
+    if (int rc = all_aligned({X, W1r, W2r, Z, H, dY, dZ, dW1r, db1r, dW2r, dXr, workspace}))
+        return rc;
+    const int64_t es = elem_size(dtype), Fs = F / T;
+    const int64_t ws_need = (db1r && N > 0) ? mlptp::colsum_workspace_bytes(N, Fs) : 0;
+    if (ws_need > 0 && (!workspace || (int64_t)workspace_bytes < ws_need))
+        return MLP_TP_E_WORKSPACE;
+    if (int rc = disjoint({{dZ, N * Fs * es}, {dW1r, D * Fs * 4}, {db1r, Fs * 4},
+                           {dW2r, Fs * D * 4}, {dXr, N * D * 4}, {workspace, ws_need}},
+                          {{X, N * D * es}, {W1r, D * Fs * es}, {W2r, Fs * D * es},
+                           {Z, N * Fs * es}, {H, N * Fs * es}, {dY, N * D * es}}))
+        return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // With N == 0 tokens dZ and dXr are empty, and the weight gradients are empty sums: the
+    // K = 0 products and the column sum below then write zeros.
+    if (N > 0) {
+        // dZ = (dY W2r^T) * phi'(Z)  [Z 06]
+        mlptp::launch_bwd_dz(dY, W2r, Z, dZ, N, D, Fs, dtype, act, s);
+        if (int rc = launch_status()) return rc;
+    }
+    // dW2r = H^T dY   [U 3.6.1]: C [Fs, D], A = H stored [N, Fs], B = dY stored [N, D]
+    mlptp::launch_wgrad(H, dY, dW2r, Fs, D, N, Fs, D, dtype, s);
+    if (int rc = launch_status()) return rc;
+    // dW1r = X^T dZ:  C [D, Fs], A = X stored [N, D], B = dZ stored [N, Fs]
+    mlptp::launch_wgrad(X, dZ, dW1r, D, Fs, N, D, Fs, dtype, s);
+    if (int rc = launch_status()) return rc;
+    if (db1r) {
+        mlptp::launch_colsum(dZ, static_cast<float*>(workspace), db1r, N, Fs, dtype, s);
+        if (int rc = launch_status()) return rc;
+    }
+    if (N > 0) {
+        // dXr = dZ W1r^T: this rank's partial of dX [Z 06 equation]
+        mlptp::launch_dx(dZ, W1r, dXr, N, D, Fs, dtype, s);
+    }
+    return launch_status();
+}
+
+const char* mlp_tp_strerror(int code)
+{
+    switch (code) {
+    case MLP_TP_OK: return "success";
+    case MLP_TP_E_NULL: return "a required pointer is NULL";
+    case MLP_TP_E_SHAPE: return "invalid size (N < 0, D <= 0, F <= 0, T out of range, or too large)";
+    case MLP_TP_E_INDIVISIBLE: return "the shard count T does not divide F";
+    case MLP_TP_E_DTYPE: return "unknown dtype code";
+    case MLP_TP_E_ACT: return "unknown activation code";
+    case MLP_TP_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case MLP_TP_E_WORKSPACE: return "workspace missing or too small";
+    case MLP_TP_E_HIP: return "a HIP kernel launch failed";
+    case MLP_TP_E_ALIAS: return "an output overlaps an input or another output";
+    default: return "unknown error code";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// bwd.hip -- backward shard kernels.
+//
+// Pages cited, as [tag section]:
+//   [Z] zwjcode.cn, "一层 MLP 太宽而放不下时怎样切？列并行、行并行与块尾归约"
+//   [U] unpurerationalist.github.io, "LLM Systems 16: Model Parallel Training"
+//   [C] charliedreemur.github.io, "TP:Column / Row Parallel Linear 怎么切? MLP 和 attention 怎么切?"
+#include "dispatch.hpp"
+#include "launch.hpp"
+
+namespace mlptp {
+
+// dH = dY W2^(r)^T (no exchange in the row-parallel backward), then dZ = dH * phi'(Z)
+// [Z 06], [U 3.6.1]. GEMM view: M = N tokens, N = Fs, K = D; A = dY (k-contiguous),
+// B(k = d, n = j) = W2r[j, d] (k-contiguous).
+void launch_bwd_dz(const void* dY, const void* W2r, const void* Z, void* dZ, int64_t N, int64_t D,
+                   int64_t Fs, int dtype, int act, hipStream_t s)
+{
+    const int vec = (Fs % 4 == 0);
+    if (dtype == kBF16) {
+        EpiActGrad<uint16_t> epi{static_cast<const uint16_t*>(Z), static_cast<uint16_t*>(dZ), Fs,
+                                 act, vec};
+        run_mfma<DefaultTile, true, true>(dY, W2r, N, Fs, D, D, D, epi, s);
+    } else {
+        EpiActGrad<float> epi{static_cast<const float*>(Z), static_cast<float*>(dZ), Fs, act, vec};
+        run_simt<true, true>(dY, W2r, N, Fs, D, D, D, epi, s);
+    }
+}
+
+// Local weight gradients [Z 06], [U 3.6.1]: C = A^T B, both operands stored token-major
+// ([K, M] and [K, N]), so both are transposed into LDS.
+void launch_wgrad(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
+                  int64_t lda, int64_t ldb, int dtype, hipStream_t s)
+{
+    EpiStoreF32 epi{C, N, (int)(N % 4 == 0)};
+    if (dtype == kBF16)
+        run_mfma<DefaultTile, false, false>(A, B, M, N, K, lda, ldb, epi, s);
+    else
+        run_simt<false, false>(A, B, M, N, K, lda, ldb, epi, s);
+}
+
+// dX^(r) = dZ W1^(r)^T, this rank's partial of the input gradient [Z 06 equation],
+// [C 推导 / 关键公式]. GEMM view: M = N tokens, N = D, K = Fs; A = dZ (k-contiguous),
+// B(k = j, n = d) = W1r[d, j] (k-contiguous).
+void launch_dx(const void* dZ, const void* W1r, float* dX, int64_t N, int64_t D, int64_t Fs,
+               int dtype, hipStream_t s)
+{
+    EpiStoreF32 epi{dX, D, (int)(D % 4 == 0)};
+    if (dtype == kBF16)
+        run_mfma<DefaultTile, true, true>(dZ, W1r, N, D, Fs, Fs, Fs, epi, s);
+    else
+        run_simt<true, true>(dZ, W1r, N, D, Fs, Fs, Fs, epi, s);
+}
+
+// db1^(r)[j] = sum over tokens of dZ[n, j]. Pass 1: each workgroup sums a 128-token slab of
+// 256 columns into ws[slab, :]; pass 2 adds the slabs in order. No atomics, so the result is
+// the same on every run.
+constexpr int kColsumRows = 128;
+
+template <class T>
+__device__ __forceinline__ float as_f32(T v);
+template <>
+__device__ __forceinline__ float as_f32<uint16_t>(uint16_t v) { return bf16_bits_to_f32(v); }
+template <>
+__device__ __forceinline__ float as_f32<float>(float v) { return v; }
+
+template <class T>
+__global__ __launch_bounds__(256) void colsum_slabs(const T* __restrict__ dZ, float* __restrict__ ws,
+                                                    int64_t N, int64_t Fs)
+{
+    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (col >= Fs) return;
+    const int64_t r0 = (int64_t)blockIdx.y * kColsumRows;
+    const int64_t r1 = (r0 + kColsumRows < N) ? r0 + kColsumRows : N;
+    float acc = 0.f;
+    for (int64_t r = r0; r < r1; ++r) acc += as_f32<T>(dZ[r * Fs + col]);
+    ws[(int64_t)blockIdx.y * Fs + col] = acc;
+}
+
+__global__ __launch_bounds__(256) void colsum_finish(const float* __restrict__ ws,
+                                                     float* __restrict__ out, int64_t slabs,
+                                                     int64_t Fs)
+{
+    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (col >= Fs) return;
+    float acc = 0.f;
+    for (int64_t b = 0; b < slabs; ++b) acc += ws[b * Fs + col];
+    out[col] = acc;
+}
+
+int64_t colsum_workspace_bytes(int64_t N, int64_t Fs)
+{
+    return ceil_div(N, kColsumRows) * Fs * (int64_t)sizeof(float);
+}
+
+void launch_colsum(const void* dZ, float* ws, float* db1, int64_t N, int64_t Fs, int dtype,
+                   hipStream_t s)
+{
+    const int64_t slabs = ceil_div(N, kColsumRows);
+    const dim3 grid1((uint32_t)ceil_div(Fs, 256), (uint32_t)slabs);
+    if (slabs == 0)
+        ;  // no tokens: the finishing pass writes zeros
+    else if (dtype == kBF16)
+        hipLaunchKernelGGL(colsum_slabs<uint16_t>, grid1, dim3(256), 0, s,
+                           static_cast<const uint16_t*>(dZ), ws, N, Fs);
+    else
+        hipLaunchKernelGGL(colsum_slabs<float>, grid1, dim3(256), 0, s,
+                           static_cast<const float*>(dZ), ws, N, Fs);
+    hipLaunchKernelGGL(colsum_finish, dim3((uint32_t)ceil_div(Fs, 256)), dim3(256), 0, s, ws, db1,
+                       slabs, Fs);
+}
+
+}  // namespace mlptp

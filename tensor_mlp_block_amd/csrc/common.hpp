@@ -1,0 +1,98 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of libmlptp.so.
+//
+// Pages cited, as [tag section]:
+//   [Z] zwjcode.cn, "一层 MLP 太宽而放不下时怎样切？列并行、行并行与块尾归约"
+//   [C] charliedreemur.github.io, "TP:Column / Row Parallel Linear 怎么切? MLP 和 attention 怎么切?"
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlptp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum ActCode : int {
+    kActIdentity = 0,
+    kActRelu = 1,
+    kActGeluTanh = 2,
+    kActGeluErf = 3,
+    kActGeluSigmoid = 4,
+};
+
+// bf16 is carried as its 16-bit pattern; widening is exact.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
+{
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// Logistic function 1 / (1 + e^-x), stable at both ends (e^-x -> inf gives 0, -> 0 gives 1).
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// GELU, tanh form: 0.5 z (1 + tanh(u)) with u = sqrt(2/pi) (z + 0.044715 z^3). Since
+// 0.5 (1 + tanh(u)) equals the logistic function at 2u, it is evaluated as z * sigmoid(2u),
+// which needs one exponential and saturates cleanly for large |z|.
+constexpr float kSqrt2OverPi = 0.7978845608028654f;
+constexpr float kTanhCubic = 0.044715f;
+constexpr float kSigmoidScale = 1.702f;
+constexpr float kInvSqrt2 = 0.7071067811865476f;
+constexpr float kInvSqrt2Pi = 0.3989422804014327f;
+
+// phi(z) [Z 02]: elementwise, so each shard applies it to its own columns with no exchange.
+__device__ __forceinline__ float act_fwd(int act, float z)
+{
+    switch (act) {
+    case kActRelu:
+        return z > 0.0f ? z : 0.0f;
+    case kActGeluTanh: {
+        float u = kSqrt2OverPi * (z + kTanhCubic * z * z * z);
+        return z * sigmoidf_(2.0f * u);
+    }
+    case kActGeluErf:
+        return 0.5f * z * (1.0f + erff(z * kInvSqrt2));
+    case kActGeluSigmoid:
+        return z * sigmoidf_(kSigmoidScale * z);
+    default:
+        return z;
+    }
+}
+
+// phi'(z), used by the backward "through the local activation" [Z 06]. ReLU'(0) = 0.
+__device__ __forceinline__ float act_grad(int act, float z)
+{
+    switch (act) {
+    case kActRelu:
+        return z > 0.0f ? 1.0f : 0.0f;
+    case kActGeluTanh: {
+        // s = sigmoid(2u) = 0.5 (1 + tanh u); 0.5 (1 - tanh^2 u) = 2 s (1 - s).
+        float u = kSqrt2OverPi * (z + kTanhCubic * z * z * z);
+        float s = sigmoidf_(2.0f * u);
+        float du = kSqrt2OverPi * (1.0f + 3.0f * kTanhCubic * z * z);
+        return s + z * 2.0f * s * (1.0f - s) * du;
+    }
+    case kActGeluErf: {
+        float cdf = 0.5f * (1.0f + erff(z * kInvSqrt2));
+        return cdf + z * kInvSqrt2Pi * __expf(-0.5f * z * z);
+    }
+    case kActGeluSigmoid: {
+        float s = sigmoidf_(kSigmoidScale * z);
+        return s + kSigmoidScale * z * s * (1.0f - s);
+    }
+    default:
+        return 1.0f;
+    }
+}
+
+__host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace mlptp

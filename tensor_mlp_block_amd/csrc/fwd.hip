@@ -1,0 +1,43 @@
+// fwd.hip -- forward shard kernels: column-parallel up-projection with fused bias and
+// activation, and row-parallel down-projection to the fp32 partial.
+//
+// Pages cited, as [tag section]:
+//   [Z] zwjcode.cn, "一层 MLP 太宽而放不下时怎样切？列并行、行并行与块尾归约"
+//   [J] jwzheng96.github.io, "张量并行 TP 与列并行 / 行并行的实现" (Megatron-LM tutorial ch. 7)
+#include "dispatch.hpp"
+#include "launch.hpp"
+
+namespace mlptp {
+
+// Z^(r) = X W1^(r) + b1^(r), H^(r) = phi(Z^(r)) [Z 02], [J 7.2 列并行].
+// GEMM view: M = N tokens, N = Fs, K = D; A = X (k-contiguous), B = W1r [D, Fs]
+// (n-contiguous, transposed into LDS).
+void launch_up_proj(const void* X, const void* W1r, const void* b1r, void* Z, void* H, int64_t N,
+                    int64_t D, int64_t Fs, int dtype, int act, hipStream_t s)
+{
+    const int vec = (Fs % 4 == 0);
+    if (dtype == kBF16) {
+        EpiBiasAct<uint16_t> epi{static_cast<const uint16_t*>(b1r), static_cast<uint16_t*>(Z),
+                                 static_cast<uint16_t*>(H), Fs, act, vec};
+        run_mfma<DefaultTile, true, false>(X, W1r, N, Fs, D, D, Fs, epi, s);
+    } else {
+        EpiBiasAct<float> epi{static_cast<const float*>(b1r), static_cast<float*>(Z),
+                              static_cast<float*>(H), Fs, act, vec};
+        run_simt<true, false>(X, W1r, N, Fs, D, D, Fs, epi, s);
+    }
+}
+
+// P^(r) = H^(r) W2^(r), fp32, no b2 [Z 02], [Z 05], [J 7.2 行并行].
+// GEMM view: M = N tokens, N = D, K = Fs; A = H (k-contiguous), B = W2r [Fs, D]
+// (n-contiguous).
+void launch_down_proj(const void* H, const void* W2r, float* P, int64_t N, int64_t D, int64_t Fs,
+                      int dtype, hipStream_t s)
+{
+    EpiStoreF32 epi{P, D, (int)(D % 4 == 0)};
+    if (dtype == kBF16)
+        run_mfma<DefaultTile, true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
+    else
+        run_simt<true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
+}
+
+}  // namespace mlptp

@@ -1,0 +1,46 @@
+// launch.hpp -- internal host launchers of libmlptp.so (not part of the C ABI).
+//
+// Every launcher assumes its arguments were validated by the C entry points (non-null,
+// 16-byte aligned, positive sizes, N > 0) and only enqueues kernels on `s`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlptp {
+
+// dtype codes as in the C header.
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+// Z = X W1r + b1r; H = phi(Z). X [N, D], W1r [D, Fs], b1r [Fs] or null, Z/H [N, Fs].
+void launch_up_proj(const void* X, const void* W1r, const void* b1r, void* Z, void* H, int64_t N,
+                    int64_t D, int64_t Fs, int dtype, int act, hipStream_t s);
+
+// P = H W2r. H [N, Fs], W2r [Fs, D], P [N, D] fp32.
+void launch_down_proj(const void* H, const void* W2r, float* P, int64_t N, int64_t D, int64_t Fs,
+                      int dtype, hipStream_t s);
+
+// dZ = (dY W2r^T) * phi'(Z). dY [N, D], W2r [Fs, D], Z/dZ [N, Fs].
+void launch_bwd_dz(const void* dY, const void* W2r, const void* Z, void* dZ, int64_t N, int64_t D,
+                   int64_t Fs, int dtype, int act, hipStream_t s);
+
+// C [M, N] fp32 = A^T B with A stored [K, M] (lda) and B stored [K, N] (ldb): the weight
+// gradients dW2r = H^T dY and dW1r = X^T dZ.
+void launch_wgrad(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
+                  int64_t lda, int64_t ldb, int dtype, hipStream_t s);
+
+// dX = dZ W1r^T. dZ [N, Fs], W1r [D, Fs], dX [N, D] fp32.
+void launch_dx(const void* dZ, const void* W1r, float* dX, int64_t N, int64_t D, int64_t Fs,
+               int dtype, hipStream_t s);
+
+// db1 [Fs] = column sums of dZ [N, Fs], deterministic two-pass through `ws`.
+int64_t colsum_workspace_bytes(int64_t N, int64_t Fs);
+void launch_colsum(const void* dZ, float* ws, float* db1, int64_t N, int64_t Fs, int dtype,
+                   hipStream_t s);
+
+// Y = ((P[0] + P[1]) + ...) + b2 over T fp32 [N, D] partials (P is a host array).
+void launch_partial_reduce(const float* const* P, int T, const void* b2, int b2_dtype, float* Y,
+                           int64_t N, int64_t D, hipStream_t s);
+
+}  // namespace mlptp

@@ -1,0 +1,109 @@
+// reduce.hip -- block-tail reduction of the row-parallel partials on one GPU.
+//
+// Pages cited, as [tag section]:
+//   [Z] zwjcode.cn, "一层 MLP 太宽而放不下时怎样切？列并行、行并行与块尾归约"
+//   [U] unpurerationalist.github.io, "LLM Systems 16: Model Parallel Training"
+//
+// Y = (((P0 + P1) + ...) + P_{T-1}) + b2: the element-wise sum an all-reduce of the
+// row-parallel outputs performs [Z 02], [Z 04], with b2 added exactly once after the sum
+// [Z 05], [U 3.8]. The work is pure streaming: T fp32 reads and one fp32 write per element,
+// so it is bound by HBM bandwidth. Each thread handles 16-byte vectors; the T loads of one
+// vector are issued back to back so T independent 16-byte requests are in flight per
+// thread, and the streaming loads/stores are marked non-temporal so they do not evict
+// anything useful from the caches.
+#include "common.hpp"
+#include "launch.hpp"
+
+#include <string.h>
+
+#define MLP_TP_MAX_REDUCE_T_INTERNAL 64
+
+namespace mlptp {
+
+struct PartialPtrs {
+    const float* p[MLP_TP_MAX_REDUCE_T_INTERNAL];
+};
+
+__device__ __forceinline__ f32x4 ld_nt(const float* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+
+__device__ __forceinline__ void st_nt(float* p, f32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+
+__device__ __forceinline__ float bias_at(const void* b2, int b2_dtype, int64_t c)
+{
+    return b2_dtype == kBF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(b2)[c])
+                             : static_cast<const float*>(b2)[c];
+}
+
+// Vector path: D % 4 == 0, so the 4 elements of a vector share one row of b2's index space.
+template <int TT>
+__global__ __launch_bounds__(256) void partial_reduce_vec(PartialPtrs P, int T, const void* b2,
+                                                          int b2_dtype, float* Y, int64_t nvec,
+                                                          int64_t D)
+{
+    const int nt = TT > 0 ? TT : T;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
+        const int64_t e = v * 4;
+        f32x4 s = ld_nt(P.p[0] + e);
+#pragma unroll
+        for (int r = 1; r < (TT > 0 ? TT : MLP_TP_MAX_REDUCE_T_INTERNAL); ++r) {
+            if (r >= nt) break;
+            s += ld_nt(P.p[r] + e);
+        }
+        if (b2) {
+            const int64_t c = e % D;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) s[q] += bias_at(b2, b2_dtype, c + q);
+        }
+        st_nt(Y + e, s);
+    }
+}
+
+// Element path for D % 4 != 0.
+__global__ __launch_bounds__(256) void partial_reduce_scalar(PartialPtrs P, int T, const void* b2,
+                                                             int b2_dtype, float* Y, int64_t n,
+                                                             int64_t D)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
+        float s = P.p[0][e];
+        for (int r = 1; r < T; ++r) s += P.p[r][e];
+        if (b2) s += bias_at(b2, b2_dtype, e % D);
+        Y[e] = s;
+    }
+}
+
+void launch_partial_reduce(const float* const* P, int T, const void* b2, int b2_dtype, float* Y,
+                           int64_t N, int64_t D, hipStream_t s)
+{
+    PartialPtrs pp;
+    memset(&pp, 0, sizeof(pp));
+    for (int r = 0; r < T; ++r) pp.p[r] = P[r];
+    const int64_t n = N * D;
+    // Enough workgroups to keep every CU's memory pipeline full, then grid-stride.
+    const int64_t max_groups = 256 * 16;
+    if (D % 4 == 0) {
+        const int64_t nvec = n / 4;
+        const int64_t groups = ceil_div(nvec, 256) < max_groups ? ceil_div(nvec, 256) : max_groups;
+        const dim3 grid((uint32_t)groups), block(256);
+        switch (T) {
+        case 1: hipLaunchKernelGGL(partial_reduce_vec<1>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D); break;
+        case 2: hipLaunchKernelGGL(partial_reduce_vec<2>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D); break;
+        case 4: hipLaunchKernelGGL(partial_reduce_vec<4>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D); break;
+        case 8: hipLaunchKernelGGL(partial_reduce_vec<8>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D); break;
+        default: hipLaunchKernelGGL(partial_reduce_vec<0>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D); break;
+        }
+    } else {
+        const int64_t groups = ceil_div(n, 256) < max_groups ? ceil_div(n, 256) : max_groups;
+        hipLaunchKernelGGL(partial_reduce_scalar, dim3((uint32_t)groups), dim3(256), 0, s, pp, T, b2,
+                           b2_dtype, Y, n, D);
+    }
+}
+
+}  // namespace mlptp

@@ -1,0 +1,165 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load and export every function include/mlp_tp.h declares, and every
+argument check must return its code before any HIP call. These calls pass fake, never
+dereferenced device addresses and are all rejected (or are N = 0 no-ops) on the host, so no
+kernel is launched.
+
+Pages cited:
+  [U] unpurerationalist.github.io, "LLM Systems 16: Model Parallel Training"
+  [C] charliedreemur.github.io, "TP:Column / Row Parallel Linear 怎么切? MLP 和 attention 怎么切?"
+  [Z] zwjcode.cn, "一层 MLP 太宽而放不下时怎样切？列并行、行并行与块尾归约"
+"""
+import os
+import subprocess
+
+import pytest
+
+from tensor_mlp_block_amd import binding as mt
+
+A = 0x10000  # fake 16-byte-aligned addresses, far apart
+B = 0x20000000
+C = 0x40000000
+Dp = 0x60000000
+E = 0x80000000
+G = 0xA0000000
+S = 0  # null stream
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mt.load()
+
+
+def test_library_exports_every_declared_function(lib):
+    declared = mt.declared_functions()
+    assert set(declared) >= {"mlp_tp_shard_fwd", "mlp_tp_partial_reduce", "mlp_tp_shard_bwd",
+                             "mlp_tp_up_proj", "mlp_tp_down_proj", "mlp_tp_strerror",
+                             "mlp_tp_shard_bwd_workspace_bytes"}
+    out = subprocess.run(["nm", "-D", "--defined-only", mt.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared:
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_library_is_built_for_gfx950():
+    # The embedded code object's target triple names the architecture it was built for.
+    with open(mt.LIB_PATH, "rb") as f:
+        assert b"amdgcn-amd-amdhsa--gfx950" in f.read()
+
+
+def test_strerror_covers_every_code(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
+        assert mt.strerror(code) and mt.strerror(code) != "unknown error code"
+    assert mt.strerror(-123) == "unknown error code"
+
+
+def _fwd(lib, **kw):
+    a = dict(X=A, W1r=B, b1r=None, W2r=C, H=Dp, Z=None, P=E, N=4, D=8, F=16, T=2,
+             dtype=mt.BF16, act=mt.ACT["gelu_tanh"])
+    a.update(kw)
+    return lib.mlp_tp_shard_fwd(a["X"], a["W1r"], a["b1r"], a["W2r"], a["H"], a["Z"], a["P"],
+                                a["N"], a["D"], a["F"], a["T"], a["dtype"], a["act"], S)
+
+
+def test_shard_fwd_argument_checks(lib):
+    assert _fwd(lib, X=None) == mt.E_NULL
+    assert _fwd(lib, W2r=None) == mt.E_NULL
+    assert _fwd(lib, P=None) == mt.E_NULL
+    assert _fwd(lib, D=0) == mt.E_SHAPE
+    assert _fwd(lib, F=0) == mt.E_SHAPE
+    assert _fwd(lib, N=-1) == mt.E_SHAPE
+    assert _fwd(lib, T=0) == mt.E_SHAPE
+    assert _fwd(lib, F=18, T=4) == mt.E_INDIVISIBLE   # the shard count must divide F [U 3.8]
+    assert _fwd(lib, dtype=2) == mt.E_DTYPE
+    assert _fwd(lib, act=7) == mt.E_ACT
+    assert _fwd(lib, X=A + 8) == mt.E_ALIGN
+    assert _fwd(lib, b1r=G + 4) == mt.E_ALIGN
+    assert _fwd(lib, H=A) == mt.E_ALIAS                # H over X
+    assert _fwd(lib, P=C) == mt.E_ALIAS                # P over W2r
+    assert _fwd(lib, Z=Dp) == mt.E_ALIAS               # Z over H
+    assert _fwd(lib, P=A + 16) == mt.E_ALIAS           # P over part of X
+    assert _fwd(lib, N=1 << 40) == mt.E_SHAPE          # too large to index safely
+
+
+def test_zero_tokens_is_a_host_noop(lib):
+    # N = 0 is valid and returns before any HIP call (this container has no GPU).
+    assert _fwd(lib, N=0) == mt.OK
+    assert lib.mlp_tp_up_proj(A, B, None, None, Dp, 0, 8, 16, 2, mt.BF16, 1, S) == mt.OK
+    assert lib.mlp_tp_down_proj(A, B, E, 0, 8, 16, 2, mt.F32, S) == mt.OK
+
+
+def test_up_and_down_proj_checks(lib):
+    assert lib.mlp_tp_up_proj(A, B, None, None, None, 4, 8, 16, 2, mt.BF16, 1, S) == mt.E_NULL
+    assert lib.mlp_tp_up_proj(A, B, None, Dp, Dp, 4, 8, 16, 2, mt.BF16, 1, S) == mt.E_ALIAS
+    assert lib.mlp_tp_up_proj(A, B, None, None, Dp, 4, 8, 16, 3, mt.BF16, 1, S) == mt.E_INDIVISIBLE
+    assert lib.mlp_tp_down_proj(A, B, A, 4, 8, 16, 2, mt.BF16, S) == mt.E_ALIAS
+    assert lib.mlp_tp_down_proj(A, B, E + 4, 4, 8, 16, 2, mt.BF16, S) == mt.E_ALIGN
+
+
+def _reduce(lib, ptrs, T=None, b2=None, b2_dtype=mt.F32, Y=G, N=4, D=8):
+    import ctypes
+    T = len(ptrs) if T is None else T
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    return lib.mlp_tp_partial_reduce(ctypes.cast(arr, ctypes.c_void_p), T, b2, b2_dtype, Y, N,
+                                     D, S)
+
+
+def test_partial_reduce_checks(lib):
+    assert lib.mlp_tp_partial_reduce(None, 2, None, 0, G, 4, 8, S) == mt.E_NULL
+    assert _reduce(lib, [A, None]) == mt.E_NULL
+    assert _reduce(lib, [A, B], T=0) == mt.E_SHAPE
+    assert _reduce(lib, [A] * 65) == mt.E_SHAPE                    # above MLP_TP_MAX_REDUCE_T
+    assert _reduce(lib, [A, B], D=0) == mt.E_SHAPE
+    assert _reduce(lib, [A, B], b2=C, b2_dtype=5) == mt.E_DTYPE
+    assert _reduce(lib, [A, B + 4]) == mt.E_ALIGN
+    assert _reduce(lib, [A, B], Y=A + 16) == mt.E_ALIAS            # partial overlap with P[0]
+    assert _reduce(lib, [A, B], b2=G) == mt.E_ALIAS                # Y over b2
+    assert _reduce(lib, [A, B], N=0) == mt.OK                      # no tokens: no-op
+    assert _reduce(lib, [A, B], Y=A, N=0) == mt.OK                 # exact in-place is allowed
+
+
+def test_workspace_query_uses_global_sizes(lib):
+    """[C 先弄清楚]: a [8192, 32768] weight split 8 ways gives [8192, 4096] per card; the
+    library derives Fs = F / T from the global F itself. The db1 workspace holds one fp32 row
+    of Fs per 128 tokens."""
+    assert lib.mlp_tp_shard_bwd_workspace_bytes(128, 8192, 32768, 8) == 4096 * 4
+    assert lib.mlp_tp_shard_bwd_workspace_bytes(4096, 8192, 28672, 8) == 32 * 3584 * 4
+    assert lib.mlp_tp_shard_bwd_workspace_bytes(300, 8, 16, 2) == 3 * 8 * 4
+    assert lib.mlp_tp_shard_bwd_workspace_bytes(0, 8, 16, 2) == 0
+    assert lib.mlp_tp_shard_bwd_workspace_bytes(4, 8, 18, 4) == mt.E_INDIVISIBLE
+    assert lib.mlp_tp_shard_bwd_workspace_bytes(4, 0, 16, 2) == mt.E_SHAPE
+
+
+def _bwd(lib, **kw):
+    a = dict(X=A, W1r=A + 0x1000, W2r=A + 0x2000, Z=A + 0x3000, H=A + 0x4000, dY=A + 0x5000,
+             dZ=B, dW1r=C, db1r=Dp, dW2r=E, dXr=G, ws=G + 0x100000, wsb=1 << 20, N=4, D=8, F=16,
+             T=2, dtype=mt.BF16, act=mt.ACT["gelu_tanh"])
+    a.update(kw)
+    return lib.mlp_tp_shard_bwd(a["X"], a["W1r"], a["W2r"], a["Z"], a["H"], a["dY"], a["dZ"],
+                                a["dW1r"], a["db1r"], a["dW2r"], a["dXr"], a["ws"], a["wsb"],
+                                a["N"], a["D"], a["F"], a["T"], a["dtype"], a["act"], S)
+
+
+def test_shard_bwd_argument_checks(lib):
+    assert _bwd(lib, dY=None) == mt.E_NULL
+    assert _bwd(lib, dXr=None) == mt.E_NULL
+    assert _bwd(lib, T=3) == mt.E_INDIVISIBLE
+    assert _bwd(lib, act=-1) == mt.E_ACT
+    assert _bwd(lib, dtype=9) == mt.E_DTYPE
+    assert _bwd(lib, dW2r=E + 8) == mt.E_ALIGN
+    assert _bwd(lib, ws=None) == mt.E_WORKSPACE
+    assert _bwd(lib, wsb=15) == mt.E_WORKSPACE
+    assert _bwd(lib, dZ=A + 0x3000) == mt.E_ALIAS     # dZ over Z
+    assert _bwd(lib, dW1r=B) == mt.E_ALIAS            # two outputs on one buffer
+    assert _bwd(lib, ws=G) == mt.E_ALIAS              # workspace over dXr
+
+
+def test_header_has_no_torch_or_hip_types():
+    with open(mt.HEADER) as f:
+        text = f.read()
+    assert "torch" not in text.lower().replace("torch's", "")
+    assert "hipStream_t" not in text.split("*/", 1)[1]  # streams travel as void*
+    assert 'extern "C"' in text
