@@ -66,6 +66,9 @@ def main() -> int:
     ap.add_argument("--no-rows", action="store_true", help="skip the extra per-row timings")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy three times, as the "
+                         "known-size reference for hardware byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -84,6 +87,15 @@ def main() -> int:
     mt.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 3 x 1 GiB read + 1 GiB write")
+        del src, dst
 
     w = workloads.LLAMA70B_SHARD_T8
     N, D, F, T, Fs = w.N, w.D, w.F, w.T, w.Fs
@@ -265,10 +277,12 @@ def cpu_baseline(Xc, W1c, b1c, W2c, w, seconds):
     W1, b1, W2 = (t.double().numpy() for t in (W1c, b1c, W2c))
     X = Xc.double().numpy()
     per_row_flop = 4.0 * w.D * w.Fs
+    # Calibrate on one row per oracle thread (the oracle spreads rows over its threads).
+    cal = max(2, min(w.N, oracle.num_threads()))
     t = time.perf_counter()
-    oracle.shard_fwd(X[:2], W1, b1, W2, 1, 0, act=w.act)
-    dt = (time.perf_counter() - t) / 2
-    rows = int(max(4, min(w.N, seconds / max(dt, 1e-6))))
+    oracle.shard_fwd(X[:cal], W1, b1, W2, 1, 0, act=w.act)
+    dt = (time.perf_counter() - t) / cal
+    rows = int(max(cal, min(w.N, seconds / max(dt, 1e-6))))
     idx = np.linspace(0, w.N - 1, rows).astype(np.int64)
     log(f"[bench] cpu baseline: {rows} rows (~{rows * dt:.1f} s)")
     t = time.perf_counter()

@@ -16,14 +16,18 @@ void launch_bwd_dz(const void* dY, const void* W2r, const void* Z, void* dZ, int
                    int64_t Fs, int dtype, int act, hipStream_t s)
 {
     const int vec = (Fs % 4 == 0);
-    if (dtype == kBF16) {
-        EpiActGrad<uint16_t> epi{static_cast<const uint16_t*>(Z), static_cast<uint16_t*>(dZ), Fs,
-                                 act, vec};
-        run_mfma<DefaultTile, true, true>(dY, W2r, N, Fs, D, D, D, epi, s);
-    } else {
-        EpiActGrad<float> epi{static_cast<const float*>(Z), static_cast<float*>(dZ), Fs, act, vec};
-        run_simt<true, true>(dY, W2r, N, Fs, D, D, D, epi, s);
-    }
+    with_act(act, [&](auto a) {
+        constexpr int ACT = decltype(a)::value;
+        if (dtype == kBF16) {
+            EpiActGrad<uint16_t, ACT> epi{static_cast<const uint16_t*>(Z),
+                                          static_cast<uint16_t*>(dZ), Fs, vec};
+            run_bf16<true, true>(dY, W2r, N, Fs, D, D, D, epi, s);
+        } else {
+            EpiActGrad<float, ACT> epi{static_cast<const float*>(Z), static_cast<float*>(dZ), Fs,
+                                       vec};
+            run_simt<true, true>(dY, W2r, N, Fs, D, D, D, epi, s);
+        }
+    });
 }
 
 // Local weight gradients [Z 06], [U 3.6.1]: C = A^T B, both operands stored token-major
@@ -33,7 +37,7 @@ void launch_wgrad(const void* A, const void* B, float* C, int64_t M, int64_t N, 
 {
     EpiStoreF32 epi{C, N, (int)(N % 4 == 0)};
     if (dtype == kBF16)
-        run_mfma<DefaultTile, false, false>(A, B, M, N, K, lda, ldb, epi, s);
+        run_bf16<false, false>(A, B, M, N, K, lda, ldb, epi, s);
     else
         run_simt<false, false>(A, B, M, N, K, lda, ldb, epi, s);
 }
@@ -46,7 +50,7 @@ void launch_dx(const void* dZ, const void* W1r, float* dX, int64_t N, int64_t D,
 {
     EpiStoreF32 epi{dX, D, (int)(D % 4 == 0)};
     if (dtype == kBF16)
-        run_mfma<DefaultTile, true, true>(dZ, W1r, N, D, Fs, Fs, Fs, epi, s);
+        run_bf16<true, true>(dZ, W1r, N, D, Fs, Fs, Fs, epi, s);
     else
         run_simt<true, true>(dZ, W1r, N, D, Fs, Fs, Fs, epi, s);
 }

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mlptp {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -49,47 +51,57 @@ constexpr float kInvSqrt2 = 0.7071067811865476f;
 constexpr float kInvSqrt2Pi = 0.3989422804014327f;
 
 // phi(z) [Z 02]: elementwise, so each shard applies it to its own columns with no exchange.
-__device__ __forceinline__ float act_fwd(int act, float z)
+// The activation is a compile-time parameter so a kernel inlines only its own form.
+template <int ACT>
+__device__ __forceinline__ float act_fwd(float z)
 {
-    switch (act) {
-    case kActRelu:
+    if constexpr (ACT == kActRelu) {
         return z > 0.0f ? z : 0.0f;
-    case kActGeluTanh: {
-        float u = kSqrt2OverPi * (z + kTanhCubic * z * z * z);
+    } else if constexpr (ACT == kActGeluTanh) {
+        const float u = kSqrt2OverPi * (z + kTanhCubic * z * z * z);
         return z * sigmoidf_(2.0f * u);
-    }
-    case kActGeluErf:
+    } else if constexpr (ACT == kActGeluErf) {
         return 0.5f * z * (1.0f + erff(z * kInvSqrt2));
-    case kActGeluSigmoid:
+    } else if constexpr (ACT == kActGeluSigmoid) {
         return z * sigmoidf_(kSigmoidScale * z);
-    default:
+    } else {
         return z;
     }
 }
 
 // phi'(z), used by the backward "through the local activation" [Z 06]. ReLU'(0) = 0.
-__device__ __forceinline__ float act_grad(int act, float z)
+template <int ACT>
+__device__ __forceinline__ float act_grad(float z)
+{
+    if constexpr (ACT == kActRelu) {
+        return z > 0.0f ? 1.0f : 0.0f;
+    } else if constexpr (ACT == kActGeluTanh) {
+        // s = sigmoid(2u) = 0.5 (1 + tanh u); 0.5 (1 - tanh^2 u) = 2 s (1 - s).
+        const float u = kSqrt2OverPi * (z + kTanhCubic * z * z * z);
+        const float s = sigmoidf_(2.0f * u);
+        const float du = kSqrt2OverPi * (1.0f + 3.0f * kTanhCubic * z * z);
+        return s + z * 2.0f * s * (1.0f - s) * du;
+    } else if constexpr (ACT == kActGeluErf) {
+        const float cdf = 0.5f * (1.0f + erff(z * kInvSqrt2));
+        return cdf + z * kInvSqrt2Pi * __expf(-0.5f * z * z);
+    } else if constexpr (ACT == kActGeluSigmoid) {
+        const float s = sigmoidf_(kSigmoidScale * z);
+        return s + kSigmoidScale * z * s * (1.0f - s);
+    } else {
+        return 1.0f;
+    }
+}
+
+// Calls f(std::integral_constant<int, ACT>) for the runtime activation code `act`.
+template <class F>
+inline void with_act(int act, F&& f)
 {
     switch (act) {
-    case kActRelu:
-        return z > 0.0f ? 1.0f : 0.0f;
-    case kActGeluTanh: {
-        // s = sigmoid(2u) = 0.5 (1 + tanh u); 0.5 (1 - tanh^2 u) = 2 s (1 - s).
-        float u = kSqrt2OverPi * (z + kTanhCubic * z * z * z);
-        float s = sigmoidf_(2.0f * u);
-        float du = kSqrt2OverPi * (1.0f + 3.0f * kTanhCubic * z * z);
-        return s + z * 2.0f * s * (1.0f - s) * du;
-    }
-    case kActGeluErf: {
-        float cdf = 0.5f * (1.0f + erff(z * kInvSqrt2));
-        return cdf + z * kInvSqrt2Pi * __expf(-0.5f * z * z);
-    }
-    case kActGeluSigmoid: {
-        float s = sigmoidf_(kSigmoidScale * z);
-        return s + kSigmoidScale * z * s * (1.0f - s);
-    }
-    default:
-        return 1.0f;
+    case kActRelu: f(std::integral_constant<int, kActRelu>{}); break;
+    case kActGeluTanh: f(std::integral_constant<int, kActGeluTanh>{}); break;
+    case kActGeluErf: f(std::integral_constant<int, kActGeluErf>{}); break;
+    case kActGeluSigmoid: f(std::integral_constant<int, kActGeluSigmoid>{}); break;
+    default: f(std::integral_constant<int, kActIdentity>{}); break;
     }
 }
 

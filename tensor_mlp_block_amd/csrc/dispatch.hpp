@@ -2,13 +2,33 @@
 #pragma once
 
 #include "epilogue.hpp"
+#include "gemm_dma.hpp"
 #include "gemm_mfma.hpp"
 #include "gemm_simt.hpp"
 
 namespace mlptp {
 
-// Tile for every bf16 product: 128 x 128 per workgroup, 4 waves of 64 x 64.
+// Fallback tile for bf16 products the direct-to-LDS kernel cannot take: 128 x 128 per
+// workgroup, 4 waves of 64 x 64.
 using DefaultTile = MfmaTile<128, 128, 2, 2>;
+
+// Main bf16 tile: 256 x 256 per workgroup, 8 waves (two per SIMD) of 64 x 128.
+using DmaDefaultTile = DmaTile<256, 256, 4, 2>;
+
+// The direct-to-LDS kernel loads whole 16-byte chunks and addresses a tile with 32-bit byte
+// offsets: every leading dimension and K must be multiples of 8 elements, the contiguous extent
+// of an m/n-contiguous operand too, and one tile's offsets must stay below 2 GiB.
+inline bool dma_eligible(bool a_kc, bool b_kc, int64_t M, int64_t N, int64_t K, int64_t lda,
+                         int64_t ldb)
+{
+    if (lda % 8 || ldb % 8 || K % 8) return false;
+    if (!a_kc && M % 8) return false;
+    if (!b_kc && N % 8) return false;
+    const int64_t limit = int64_t(1) << 31;
+    const int64_t span_a = a_kc ? 256 * lda * 2 : 64 * lda * 2;
+    const int64_t span_b = b_kc ? 256 * ldb * 2 : 64 * ldb * 2;
+    return span_a < limit && span_b < limit;
+}
 
 template <class Cfg, bool A_KC, bool B_KC, class Epi>
 inline void run_mfma(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int64_t lda,
@@ -19,6 +39,28 @@ inline void run_mfma(const void* A, const void* B, int64_t M, int64_t N, int64_t
     hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, A_KC, B_KC, Epi>), dim3((uint32_t)tiles),
                        dim3(Cfg::NTHREADS), 0, s, static_cast<const uint16_t*>(A),
                        static_cast<const uint16_t*>(B), M, N, K, lda, ldb, vecA, vecB, epi);
+}
+
+template <class Cfg, bool A_KC, bool B_KC, class Epi>
+inline void run_dma(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int64_t lda,
+                    int64_t ldb, Epi epi, hipStream_t s)
+{
+    const int64_t tiles = ceil_div(M, Cfg::BM) * ceil_div(N, Cfg::BN);
+    hipLaunchKernelGGL((gemm_bf16_dma<Cfg, A_KC, B_KC, Epi>), dim3((uint32_t)tiles),
+                       dim3(Cfg::NTHREADS), 0, s, static_cast<const uint16_t*>(A),
+                       static_cast<const uint16_t*>(B), M, N, K, lda, ldb, epi);
+}
+
+// Every bf16 product goes through here: the direct-to-LDS kernel when the shape allows it,
+// else the register-staged kernel.
+template <bool A_KC, bool B_KC, class Epi>
+inline void run_bf16(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int64_t lda,
+                     int64_t ldb, Epi epi, hipStream_t s)
+{
+    if (dma_eligible(A_KC, B_KC, M, N, K, lda, ldb))
+        run_dma<DmaDefaultTile, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s);
+    else
+        run_mfma<DefaultTile, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s);
 }
 
 template <bool A_KC, bool B_KC, class Epi>

@@ -84,13 +84,12 @@ struct EpiStoreF32 {
 
 // Up-projection epilogue [Z 02], [Z 05]: z = acc + b1^(r)[col] (the bias slice that travels
 // with W1's columns), optional store of Z for the backward, H = phi(z). One HBM write each.
-template <class T>
+template <class T, int ACT>
 struct EpiBiasAct {
     const T* bias;  // [N] or nullptr
     T* Z;           // [M, N] or nullptr
     T* H;           // [M, N]
     int64_t ldc;
-    int act;
     int vec;
     __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 v, int64_t M,
                                                int64_t N) const
@@ -101,19 +100,18 @@ struct EpiBiasAct {
         if (Z) store4(Z + row * ldc + col, v, n, vec);
         f32x4 h;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = act_fwd(act, v[e]);
+        for (int e = 0; e < 4; ++e) h[e] = act_fwd<ACT>(v[e]);
         store4(H + row * ldc + col, h, n, vec);
     }
 };
 
 // Backward through the local activation [Z 06], [U 3.6.1]: dZ = dH * phi'(Z), where the
 // GEMM produced dH = dY W2^(r)^T.
-template <class T>
+template <class T, int ACT>
 struct EpiActGrad {
     const T* Z;  // [M, N]
     T* dZ;       // [M, N]
     int64_t ldc;
-    int act;
     int vec;
     __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 v, int64_t M,
                                                int64_t N) const
@@ -123,7 +121,7 @@ struct EpiActGrad {
         const f32x4 z = load4(Z + row * ldc + col, n, vec);
         f32x4 d;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = v[e] * act_grad(act, z[e]);
+        for (int e = 0; e < 4; ++e) d[e] = v[e] * act_grad<ACT>(z[e]);
         store4(dZ + row * ldc + col, d, n, vec);
     }
 };

@@ -16,15 +16,19 @@ void launch_up_proj(const void* X, const void* W1r, const void* b1r, void* Z, vo
                     int64_t D, int64_t Fs, int dtype, int act, hipStream_t s)
 {
     const int vec = (Fs % 4 == 0);
-    if (dtype == kBF16) {
-        EpiBiasAct<uint16_t> epi{static_cast<const uint16_t*>(b1r), static_cast<uint16_t*>(Z),
-                                 static_cast<uint16_t*>(H), Fs, act, vec};
-        run_mfma<DefaultTile, true, false>(X, W1r, N, Fs, D, D, Fs, epi, s);
-    } else {
-        EpiBiasAct<float> epi{static_cast<const float*>(b1r), static_cast<float*>(Z),
-                              static_cast<float*>(H), Fs, act, vec};
-        run_simt<true, false>(X, W1r, N, Fs, D, D, Fs, epi, s);
-    }
+    with_act(act, [&](auto a) {
+        constexpr int ACT = decltype(a)::value;
+        if (dtype == kBF16) {
+            EpiBiasAct<uint16_t, ACT> epi{static_cast<const uint16_t*>(b1r),
+                                          static_cast<uint16_t*>(Z), static_cast<uint16_t*>(H),
+                                          Fs, vec};
+            run_bf16<true, false>(X, W1r, N, Fs, D, D, Fs, epi, s);
+        } else {
+            EpiBiasAct<float, ACT> epi{static_cast<const float*>(b1r), static_cast<float*>(Z),
+                                       static_cast<float*>(H), Fs, vec};
+            run_simt<true, false>(X, W1r, N, Fs, D, D, Fs, epi, s);
+        }
+    });
 }
 
 // P^(r) = H^(r) W2^(r), fp32, no b2 [Z 02], [Z 05], [J 7.2 行并行].
@@ -35,7 +39,7 @@ void launch_down_proj(const void* H, const void* W2r, float* P, int64_t N, int64
 {
     EpiStoreF32 epi{P, D, (int)(D % 4 == 0)};
     if (dtype == kBF16)
-        run_mfma<DefaultTile, true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
+        run_bf16<true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
     else
         run_simt<true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
 }

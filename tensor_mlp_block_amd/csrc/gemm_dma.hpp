@@ -1,0 +1,268 @@
+// gemm_dma.hpp -- bf16 MFMA GEMM for gfx950 with direct global->LDS loads and LDS transpose
+// reads, fp32 accumulation.
+//
+// Same contract as gemm_mfma.hpp (C[M, N] = sum_k A(m, k) B(k, n), layouts A_KC / B_KC,
+// results handed to an epilogue functor), for the common case where every leading dimension,
+// K, and the m/n extent of an m/n-contiguous operand are multiples of 8.
+//
+// How the operands reach the matrix cores:
+//   * Global -> LDS with `buffer_load_dwordx4 ... lds`: each wave instruction moves 64 x 16
+//     bytes straight into a contiguous 1 KB of LDS (lane l's 16 bytes land at offset 16 l), with
+//     no register round trip. Out-of-range lanes get an offset past the buffer's range, and the
+//     hardware range check writes zeros for them, so ragged tiles need no branches.
+//   * A k-contiguous operand is stored [rows][64 k] (128 bytes per row); an m/n-contiguous one
+//     keeps its global orientation, [64 k][rows]. In both, 16-byte chunks are XOR-swizzled with
+//     bits of the row (k) index; the swizzle is applied on the global side by choosing which
+//     chunk each lane fetches, since the LDS side of the load is fixed by the lane number.
+//   * MFMA operands (16 rows x 32 k, 8 k-values per lane) are read with one ds_read_b128 from a
+//     k-contiguous tile, or with two ds_read_b64_tr_b16 from a [k][rows] tile: in each 16-lane
+//     group the transpose read returns lane i the i-th element of the four 16-element rows the
+//     group's lanes address, i.e. 4 consecutive k of one output row.
+//   * Two LDS stages: loads of stage k+1 are issued before the MFMAs of stage k; a vmcnt wait
+//     and one barrier end each stage.
+#pragma once
+
+#include "common.hpp"
+
+namespace mlptp {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define MLPTP_LDS __attribute__((address_space(3)))
+
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4 rsrc, MLPTP_LDS uint32_t* lds,
+                                                           int size, int voffset, int soffset,
+                                                           int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer resource over [base, base + 2 GiB): offsets >= 0x80000000 are out of range and load
+// zeros. Word 3 is the gfx9-family default (32-bit dword format, no swizzle).
+__device__ __forceinline__ i32x4 make_buffer_rsrc(const void* base)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a & 0xffffffffu));
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xffffu));
+    r[2] = (int)0x80000000u;
+    r[3] = 0x00020000;
+    return r;
+}
+
+constexpr int kOutOfRange = (int)0x80000000u;
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int GROUP_M_ = 4>
+struct DmaTile {
+    static constexpr int BM = BM_, BN = BN_, BK = 64;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int NWAVES = WAVES_M * WAVES_N;
+    static constexpr int NTHREADS = NWAVES * 64;
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    static constexpr int FM = WTM / 16, FN = WTN / 16;
+    static constexpr int KSUB = BK / 32;
+    static constexpr int GROUP_M = GROUP_M_;
+    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "tiles move in 1 KB wave loads");
+};
+
+// k-contiguous tile [rows][64]: chunk c (8 elements) of row r sits at physical chunk
+// c ^ kc_swz(r). Spreads 16 consecutive rows of one chunk over distinct banks.
+__device__ __forceinline__ int kc_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+// [64][rows] tile: 16-byte chunk c of k-row k sits at c ^ mc_swz(k). Four consecutive k rows
+// (one transpose read) and the rows 8 apart (the next lane group) land on distinct banks.
+template <int ROWS>
+__device__ __forceinline__ int mc_swz(int k)
+{
+    if constexpr (ROWS >= 128)
+        return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
+    else
+        return (k & 3) << 1;
+}
+
+// Issues this wave's share of the global->LDS copy of one operand tile (ROWS x 64 k).
+//   KC: element (row, k) at src[row * ld + k]; LDS [ROWS][64].
+//   MC: element (row, k) at src[k * ld + row]; LDS [64][ROWS].
+// `src` already points at (row0, k0); rows >= rows_left or k >= k_left load zeros.
+template <int ROWS, int NWAVES, bool KC>
+__device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t ld, int rows_left,
+                                         int k_left, MLPTP_LDS uint8_t* lds, int wave, int lane)
+{
+    const i32x4 rsrc = make_buffer_rsrc(src);
+    constexpr int kInstr = ROWS * 64 * 2 / 1024;  // 1 KB wave loads per tile
+    static_assert(kInstr % NWAVES == 0, "tile does not split evenly over the waves");
+#pragma unroll
+    for (int q = 0; q < kInstr / NWAVES; ++q) {
+        const int qi = q * NWAVES + wave;
+        int off;
+        if (KC) {
+            const int r = qi * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ kc_swz(r);
+            const bool ok = r < rows_left && c * 8 < k_left;
+            off = ok ? (int)(r * ld * 2 + c * 16) : kOutOfRange;
+        } else {
+            constexpr int kRowsPerInstr = 1024 / (ROWS * 2);
+            constexpr int kChunks = ROWS / 8;
+            const int k = qi * kRowsPerInstr + lane / kChunks;
+            const int c = (lane % kChunks) ^ mc_swz<ROWS>(k);
+            const bool ok = k < k_left && c * 8 < rows_left;
+            off = ok ? (int)(k * ld * 2 + c * 16) : kOutOfRange;
+        }
+        llvm_amdgcn_raw_buffer_load_lds(rsrc, reinterpret_cast<MLPTP_LDS uint32_t*>(lds + qi * 1024),
+                                        16, off, 0, 0, 0);
+    }
+}
+
+// One MFMA operand fragment (16 rows x 32 k) for k-step ks from a KC tile.
+template <int ROWS>
+__device__ __forceinline__ bf16x8 frag_kc(const MLPTP_LDS uint8_t* lds, int row0, int ks, int lane)
+{
+    const int r = row0 + (lane & 15);
+    const int c = (ks * 4 + (lane >> 4)) ^ kc_swz(r);
+    return *reinterpret_cast<const MLPTP_LDS bf16x8*>(lds + r * 128 + c * 16);
+}
+
+// The same fragment from an MC tile [64][ROWS] with two transpose reads: lane (16 g + i) gets
+// k = 32 ks + 8 g + {0..3} from the first read and {4..7} from the second, of row row0 + i.
+template <int ROWS>
+__device__ __forceinline__ bf16x8 frag_mc(const MLPTP_LDS uint8_t* lds, int row0, int ks, int lane)
+{
+    const int g = lane >> 4, i = lane & 15;
+    const int n = row0 + 4 * (i & 3);
+    s16x4 h[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int k = ks * 32 + 8 * g + 4 * t + (i >> 2);
+        const int c = (n >> 3) ^ mc_swz<ROWS>(k);
+        const MLPTP_LDS uint8_t* p = lds + k * (ROWS * 2) + c * 16 + (n & 7) * 2;
+        h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<MLPTP_LDS s16x4*>(const_cast<MLPTP_LDS uint8_t*>(p)));
+    }
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int GROUP_M>
+__device__ __forceinline__ void dma_tile_coords(int64_t bid, int64_t tiles_m, int64_t tiles_n,
+                                                int64_t& tm, int64_t& tn)
+{
+    const int64_t ntiles = tiles_m * tiles_n;
+    constexpr int kXcds = 8;
+    if (ntiles % kXcds == 0) bid = (bid % kXcds) * (ntiles / kXcds) + bid / kXcds;
+    const int64_t per_group = (int64_t)GROUP_M * tiles_n;
+    const int64_t group = bid / per_group;
+    const int64_t first_m = group * GROUP_M;
+    const int64_t gm = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+    const int64_t in_group = bid % per_group;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}
+
+struct DmaCtx {
+    const uint16_t* A;
+    const uint16_t* B;
+    int64_t M, N, K, lda, ldb, m0, n0;
+    int m_left, n_left, wave, lane;
+};
+
+template <class Cfg, bool A_KC, bool B_KC>
+__device__ __forceinline__ void dma_issue(const DmaCtx& c, int64_t kt, MLPTP_LDS uint8_t* base)
+{
+    const int64_t k0 = kt * Cfg::BK;
+    const int k_left = (int)((c.K - k0) < Cfg::BK ? (c.K - k0) : Cfg::BK);
+    const uint16_t* a = A_KC ? c.A + c.m0 * c.lda + k0 : c.A + k0 * c.lda + c.m0;
+    const uint16_t* b = B_KC ? c.B + c.n0 * c.ldb + k0 : c.B + k0 * c.ldb + c.n0;
+    dma_tile<Cfg::BM, Cfg::NWAVES, A_KC>(a, c.lda, c.m_left, k_left, base, c.wave, c.lane);
+    dma_tile<Cfg::BN, Cfg::NWAVES, B_KC>(b, c.ldb, c.n_left, k_left, base + Cfg::A_BYTES, c.wave,
+                                         c.lane);
+}
+
+// One pipeline step: start the loads of stage `next_kt` (if >= 0) into `nxt`, then run the
+// MFMAs of the stage held in `cur`. `cur` and `nxt` are distinct stages; the __restrict__
+// qualifiers tell the compiler so, which lets it read `cur` while the loads into `nxt` are
+// still in flight instead of waiting for them first.
+template <class Cfg, bool A_KC, bool B_KC>
+__device__ __attribute__((always_inline)) inline void dma_step(
+    const DmaCtx& c, int64_t next_kt, const MLPTP_LDS uint8_t* __restrict__ cur,
+    MLPTP_LDS uint8_t* __restrict__ nxt, f32x4 (&acc)[Cfg::FM][Cfg::FN], int wm, int wn)
+{
+    if (next_kt >= 0) dma_issue<Cfg, A_KC, B_KC>(c, next_kt, nxt);
+    const MLPTP_LDS uint8_t* As = cur;
+    const MLPTP_LDS uint8_t* Bs = cur + Cfg::A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < Cfg::KSUB; ++ks) {
+        bf16x8 af[Cfg::FM], bfr[Cfg::FN];
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i) {
+            const int row = wm * Cfg::WTM + i * 16;
+            af[i] = A_KC ? frag_kc<Cfg::BM>(As, row, ks, c.lane) : frag_mc<Cfg::BM>(As, row, ks, c.lane);
+        }
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) {
+            const int row = wn * Cfg::WTN + j * 16;
+            bfr[j] = B_KC ? frag_kc<Cfg::BN>(Bs, row, ks, c.lane) : frag_mc<Cfg::BN>(Bs, row, ks, c.lane);
+        }
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    }
+}
+
+template <class Cfg, bool A_KC, bool B_KC, class Epi>
+__global__ __launch_bounds__(Cfg::NTHREADS, 1) void gemm_bf16_dma(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int64_t M, int64_t N,
+    int64_t K, int64_t lda, int64_t ldb, Epi epi)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * Cfg::STAGE_BYTES];
+    // C-style cast: generic -> LDS address space (smem_raw is an LDS variable).
+    MLPTP_LDS uint8_t* smem = (MLPTP_LDS uint8_t*)(smem_raw);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave % Cfg::WAVES_M, wn = wave / Cfg::WAVES_M;
+
+    const int64_t tiles_m = ceil_div(M, Cfg::BM), tiles_n = ceil_div(N, Cfg::BN);
+    int64_t tm, tn;
+    dma_tile_coords<Cfg::GROUP_M>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+    const int m_left = (int)((M - m0) < Cfg::BM ? (M - m0) : Cfg::BM);
+    const int n_left = (int)((N - n0) < Cfg::BN ? (N - n0) : Cfg::BN);
+
+    f32x4 acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t nk = ceil_div(K, Cfg::BK);
+    const DmaCtx ctx{A, B, M, N, K, lda, ldb, m0, n0, m_left, n_left, wave, lane};
+
+    dma_issue<Cfg, A_KC, B_KC>(ctx, 0, smem);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        MLPTP_LDS uint8_t* cur = smem + (kt & 1) * Cfg::STAGE_BYTES;
+        MLPTP_LDS uint8_t* nxt = smem + ((kt + 1) & 1) * Cfg::STAGE_BYTES;
+        dma_step<Cfg, A_KC, B_KC>(ctx, kt + 1 < nk ? kt + 1 : -1, cur, nxt, acc, wm, wn);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the next stage
+        __syncthreads();
+    }
+
+    const int frow = lane & 15, fchunk = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+        const int64_t row = m0 + wm * Cfg::WTM + i * 16 + frow;
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) {
+            const int64_t col = n0 + wn * Cfg::WTN + j * 16 + 4 * fchunk;
+            epi(row, col, acc[i][j], M, N);
+        }
+    }
+}
+
+}  // namespace mlptp
