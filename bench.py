@@ -28,8 +28,6 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "TP-shard MLP fwd TFLOP/s + % bf16 MFMA peak (D=8192, F/T=3584, N=4096)"
-KERNEL_SOURCES = ("gemm_mfma.hpp", "epilogue.hpp", "dispatch.hpp", "fwd.hip", "common.hpp",
-                  "reduce.hip", "bwd.hip")
 
 
 def log(msg: str) -> None:
@@ -37,9 +35,13 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
+    """Hash of every HIP source of the library: a counter record is valid only for these."""
+    import glob
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "tensor_mlp_block_amd", "csrc", name), "rb") as f:
+    csrc = os.path.join(ROOT, "tensor_mlp_block_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 

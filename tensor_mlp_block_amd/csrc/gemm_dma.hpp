@@ -70,12 +70,20 @@ struct DmaTile {
 // c ^ kc_swz(r). Spreads 16 consecutive rows of one chunk over distinct banks.
 __device__ __forceinline__ int kc_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
-// [64][rows] tile: 16-byte chunk c of k-row k sits at c ^ mc_swz(k). Four consecutive k rows
-// (one transpose read) and the rows 8 apart (the next lane group) land on distinct banks.
+// [64][rows] tile: 16-byte chunk c of k-row k sits at c ^ mc_swz(k). A transpose read touches
+// four consecutive k rows (32 bytes each) per 16-lane group, and the next group reads the rows
+// 8 below; the swizzle puts all of them on distinct banks.
+//   * ROWS a power of two >= 128: rows are a multiple of 256 bytes apart, so every k row starts
+//     on the same bank; XOR the chunk pair with k mod 4 and flip bit 3 with bit 3 of k.
+//   * ROWS = 224: a 448-byte row pitch already spreads 4 consecutive rows over distinct banks;
+//     only rows 8 apart collide, so flip chunk bit 1 with bit 3 of k (stays inside the row's
+//     28 chunks, since it permutes within aligned groups of 4).
 template <int ROWS>
 __device__ __forceinline__ int mc_swz(int k)
 {
-    if constexpr (ROWS >= 128)
+    if constexpr (ROWS == 224)
+        return ((k >> 3) & 1) << 1;
+    else if constexpr (ROWS >= 128)
         return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
     else
         return (k & 3) << 1;
@@ -84,31 +92,37 @@ __device__ __forceinline__ int mc_swz(int k)
 // Issues this wave's share of the global->LDS copy of one operand tile (ROWS x 64 k).
 //   KC: element (row, k) at src[row * ld + k]; LDS [ROWS][64].
 //   MC: element (row, k) at src[k * ld + row]; LDS [64][ROWS].
-// `src` already points at (row0, k0); rows >= rows_left or k >= k_left load zeros.
+// `src` already points at (row0, k0); rows >= rows_left or k >= k_left load zeros. The first
+// row (KC) or k row (MC) of each 1 KB load goes into the scalar buffer base, so the per-lane
+// offset only holds the row within the load and the swizzled chunk: few live registers.
 template <int ROWS, int NWAVES, bool KC>
 __device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t ld, int rows_left,
                                          int k_left, MLPTP_LDS uint8_t* lds, int wave, int lane)
 {
-    const i32x4 rsrc = make_buffer_rsrc(src);
     constexpr int kInstr = ROWS * 64 * 2 / 1024;  // 1 KB wave loads per tile
     static_assert(kInstr % NWAVES == 0, "tile does not split evenly over the waves");
 #pragma unroll
     for (int q = 0; q < kInstr / NWAVES; ++q) {
         const int qi = q * NWAVES + wave;
         int off;
+        int first;  // first row (KC) or k row (MC) of this load
         if (KC) {
-            const int r = qi * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ kc_swz(r);
-            const bool ok = r < rows_left && c * 8 < k_left;
-            off = ok ? (int)(r * ld * 2 + c * 16) : kOutOfRange;
+            first = qi * 8;
+            const int rl = lane >> 3;
+            const int c = (lane & 7) ^ kc_swz(first + rl);
+            const bool ok = rl < rows_left - first && c * 8 < k_left;
+            off = ok ? (int)(rl * ld * 2 + c * 16) : kOutOfRange;
         } else {
-            constexpr int kRowsPerInstr = 1024 / (ROWS * 2);
+            // Chunk index idx = 64 qi + lane lands at byte 16 idx = k * 2 ROWS + 16 p.
             constexpr int kChunks = ROWS / 8;
-            const int k = qi * kRowsPerInstr + lane / kChunks;
-            const int c = (lane % kChunks) ^ mc_swz<ROWS>(k);
+            first = (qi * 64) / kChunks;
+            const int idx = qi * 64 + lane;
+            const int k = idx / kChunks;
+            const int c = (idx % kChunks) ^ mc_swz<ROWS>(k);
             const bool ok = k < k_left && c * 8 < rows_left;
-            off = ok ? (int)(k * ld * 2 + c * 16) : kOutOfRange;
+            off = ok ? (int)((k - first) * ld * 2 + c * 16) : kOutOfRange;
         }
+        const i32x4 rsrc = make_buffer_rsrc(src + (int64_t)first * ld);
         llvm_amdgcn_raw_buffer_load_lds(rsrc, reinterpret_cast<MLPTP_LDS uint32_t*>(lds + qi * 1024),
                                         16, off, 0, 0, 0);
     }
