@@ -12,8 +12,22 @@ namespace mlptp {
 // workgroup, 4 waves of 64 x 64.
 using DefaultTile = MfmaTile<128, 128, 2, 2>;
 
-// Main bf16 tile: 256 x 256 per workgroup, 8 waves (two per SIMD) of 64 x 128.
-using DmaDefaultTile = DmaTile<256, 256, 4, 2>;
+// Main bf16 tiles: 8 waves per workgroup (two per SIMD). 256 x 256 (waves of 64 x 128) by
+// default; 256 x 224 (64 x 112) and 224 x 256 (112 x 64) when an extent is a multiple of 224 and
+// that tile count fills the GPU's compute units better (e.g. F/T = 3584 = 16 x 224: 256 tiles
+// instead of 224 on 256 CUs).
+using DmaTile256x256 = DmaTile<256, 256, 4, 2>;
+using DmaTile256x224 = DmaTile<256, 224, 4, 2>;
+using DmaTile224x256 = DmaTile<224, 256, 2, 4>;
+
+int compute_units();  // of the current device, queried once
+
+// Estimated cost of a tile shape: rounds of workgroups over the CUs times the tile area.
+inline int64_t tile_cost(int64_t M, int64_t N, int bm, int bn)
+{
+    const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
+    return ceil_div(tiles, compute_units()) * bm * bn;
+}
 
 // The direct-to-LDS kernel loads whole 16-byte chunks and addresses a tile with 32-bit byte
 // offsets: every leading dimension and K must be multiples of 8 elements, the contiguous extent
@@ -57,9 +71,17 @@ template <bool A_KC, bool B_KC, class Epi>
 inline void run_bf16(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int64_t lda,
                      int64_t ldb, Epi epi, hipStream_t s)
 {
-    if (dma_eligible(A_KC, B_KC, M, N, K, lda, ldb))
-        run_dma<DmaDefaultTile, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s);
-    else
+    if (dma_eligible(A_KC, B_KC, M, N, K, lda, ldb)) {
+        const int64_t c256 = tile_cost(M, N, 256, 256);
+        const int64_t c224n = (N % 224 == 0) ? tile_cost(M, N, 256, 224) : INT64_MAX;
+        const int64_t c224m = (M % 224 == 0) ? tile_cost(M, N, 224, 256) : INT64_MAX;
+        if (c224n < c256 && c224n <= c224m)
+            run_dma<DmaTile256x224, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s);
+        else if (c224m < c256)
+            run_dma<DmaTile224x256, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s);
+        else
+            run_dma<DmaTile256x256, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s);
+    } else
         run_mfma<DefaultTile, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s);
 }
 

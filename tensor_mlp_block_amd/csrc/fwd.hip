@@ -9,6 +9,21 @@
 
 namespace mlptp {
 
+int compute_units()
+{
+    static int cus = 0;  // queried once; the first device asked for sizes every launch
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            n > 0)
+            cus = n;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
 // Z^(r) = X W1^(r) + b1^(r), H^(r) = phi(Z^(r)) [Z 02], [J 7.2 列并行].
 // GEMM view: M = N tokens, N = Fs, K = D; A = X (k-contiguous), B = W1r [D, Fs]
 // (n-contiguous, transposed into LDS).

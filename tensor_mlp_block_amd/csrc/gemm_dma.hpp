@@ -64,6 +64,7 @@ struct DmaTile {
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "tiles move in 1 KB wave loads");
+    static_assert(2 * STAGE_BYTES <= 160 * 1024, "two stages must fit in LDS");
 };
 
 // k-contiguous tile [rows][64]: chunk c (8 elements) of row r sits at physical chunk
@@ -92,18 +93,21 @@ __device__ __forceinline__ int mc_swz(int k)
 // Issues this wave's share of the global->LDS copy of one operand tile (ROWS x 64 k).
 //   KC: element (row, k) at src[row * ld + k]; LDS [ROWS][64].
 //   MC: element (row, k) at src[k * ld + row]; LDS [64][ROWS].
-// `src` already points at (row0, k0); rows >= rows_left or k >= k_left load zeros. The first
-// row (KC) or k row (MC) of each 1 KB load goes into the scalar buffer base, so the per-lane
-// offset only holds the row within the load and the swizzled chunk: few live registers.
+// `src` already points at (row0, k0); rows >= rows_left or k >= k_left load zeros. One buffer
+// resource covers the tile; the first row (KC) or k row (MC) of each 1 KB load travels in the
+// scalar offset operand, so the per-lane offset only holds the row within the load and the
+// swizzled chunk. (Out-of-range lanes carry an offset of 2^31 in the vector operand, past the
+// resource's range whether or not the hardware adds the scalar offset before its check.)
 template <int ROWS, int NWAVES, bool KC>
 __device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t ld, int rows_left,
                                          int k_left, MLPTP_LDS uint8_t* lds, int wave, int lane)
 {
     constexpr int kInstr = ROWS * 64 * 2 / 1024;  // 1 KB wave loads per tile
-    static_assert(kInstr % NWAVES == 0, "tile does not split evenly over the waves");
+    const i32x4 rsrc = make_buffer_rsrc(src);
 #pragma unroll
-    for (int q = 0; q < kInstr / NWAVES; ++q) {
+    for (int q = 0; q < (kInstr + NWAVES - 1) / NWAVES; ++q) {
         const int qi = q * NWAVES + wave;
+        if (kInstr % NWAVES != 0 && qi >= kInstr) break;  // wave-uniform
         int off;
         int first;  // first row (KC) or k row (MC) of this load
         if (KC) {
@@ -122,9 +126,9 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t ld, int ro
             const bool ok = k < k_left && c * 8 < rows_left;
             off = ok ? (int)((k - first) * ld * 2 + c * 16) : kOutOfRange;
         }
-        const i32x4 rsrc = make_buffer_rsrc(src + (int64_t)first * ld);
+        const int soff = __builtin_amdgcn_readfirstlane((int)(first * ld * 2));
         llvm_amdgcn_raw_buffer_load_lds(rsrc, reinterpret_cast<MLPTP_LDS uint32_t*>(lds + qi * 1024),
-                                        16, off, 0, 0, 0);
+                                        16, off, soff, 0, 0);
     }
 }
 

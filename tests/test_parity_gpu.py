@@ -230,6 +230,8 @@ RAGGED = [
     # no biases
     Workload("nobias_n128_d128_f256_t2", 128, 128, 256, 2, "gelu_tanh", "bf16", 7007, "normal",
              bias=False),
+    # widths that are multiples of 224: the 256x224 and 224x256 tiles, with a ragged token tail
+    Workload("tile224_n300_d448_f896_t2", 300, 448, 896, 2, "gelu_tanh", "bf16", 7008, "normal"),
 ]
 
 
