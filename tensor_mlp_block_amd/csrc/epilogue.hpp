@@ -4,9 +4,14 @@
 //   [Z] zwjcode.cn, "一层 MLP 太宽而放不下时怎样切？列并行、行并行与块尾归约"
 //   [U] unpurerationalist.github.io, "LLM Systems 16: Model Parallel Training"
 //
-// Each functor receives four consecutive fp32 results C[row, col .. col+3] (col % 4 == 0) and
-// the GEMM extent; it writes nothing outside [0, M) x [0, N). `vec` says the output row
-// stride allows one vector store per four elements.
+// Each functor handles four consecutive fp32 results C[row, col .. col+3] (col % 4 == 0) and
+// writes nothing outside [0, M) x [0, N); `vec` says the output row stride allows one vector
+// store per four elements. The work is split in three so that a kernel can issue every load an
+// epilogue needs before its first store:
+//   col_load(col, N)          data that depends on the column only (a bias slice);
+//   elem_load(row, col, M, N) data per element (a saved activation input);
+//   apply(row, col, v, c, e, M, N) the arithmetic and the stores.
+// operator() runs the three in order, for kernels that do not stage the loads.
 #pragma once
 
 #include "common.hpp"
@@ -62,6 +67,51 @@ __device__ __forceinline__ void store4(uint16_t* p, f32x4 v, int n, bool vec)
         if (e < n) p[e] = f32_to_bf16_bits(v[e]);
 }
 
+// Four bf16 values kept packed (two dwords) between a load and its use.
+struct Bf16x4 {
+    uint32_t lo, hi;
+};
+
+__device__ __forceinline__ Bf16x4 load4_raw(const uint16_t* p, int n, bool vec)
+{
+    if (vec && n == 4) {
+        const uint2 w = *reinterpret_cast<const uint2*>(p);
+        return Bf16x4{w.x, w.y};
+    }
+    uint16_t e[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (i < n) e[i] = p[i];
+    return Bf16x4{(uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16)};
+}
+
+__device__ __forceinline__ f32x4 unpack4(Bf16x4 w)
+{
+    return f32x4{bf16_bits_to_f32(w.lo & 0xffffu), bf16_bits_to_f32(w.lo >> 16),
+                 bf16_bits_to_f32(w.hi & 0xffffu), bf16_bits_to_f32(w.hi >> 16)};
+}
+
+// Storage of four staged values of type T: packed bf16, or fp32.
+template <class T> struct Staged4;
+template <> struct Staged4<uint16_t> {
+    Bf16x4 raw;
+    __device__ __forceinline__ static Staged4 load(const uint16_t* p, int n, bool vec)
+    {
+        return Staged4{load4_raw(p, n, vec)};
+    }
+    __device__ __forceinline__ f32x4 get() const { return unpack4(raw); }
+};
+template <> struct Staged4<float> {
+    f32x4 raw;
+    __device__ __forceinline__ static Staged4 load(const float* p, int n, bool vec)
+    {
+        return Staged4{load4(p, n, vec)};
+    }
+    __device__ __forceinline__ f32x4 get() const { return raw; }
+};
+
+struct NoData {};
+
 __device__ __forceinline__ int valid4(int64_t row, int64_t col, int64_t M, int64_t N)
 {
     if (row >= M || col >= N) return 0;
@@ -74,11 +124,24 @@ struct EpiStoreF32 {
     float* C;
     int64_t ldc;
     int vec;
-    __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 v, int64_t M,
-                                               int64_t N) const
+    using ColData = NoData;
+    using ElemData = NoData;
+    static constexpr bool kColData = false, kElemData = false;
+    __device__ __forceinline__ ColData col_load(int64_t, int64_t) const { return {}; }
+    __device__ __forceinline__ ElemData elem_load(int64_t, int64_t, int64_t, int64_t) const
+    {
+        return {};
+    }
+    __device__ __forceinline__ void apply(int64_t row, int64_t col, f32x4 v, ColData, ElemData,
+                                          int64_t M, int64_t N) const
     {
         const int n = valid4(row, col, M, N);
         if (n) store4(C + row * ldc + col, v, n, vec);
+    }
+    __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 v, int64_t M,
+                                               int64_t N) const
+    {
+        apply(row, col, v, {}, {}, M, N);
     }
 };
 
@@ -91,17 +154,37 @@ struct EpiBiasAct {
     T* H;           // [M, N]
     int64_t ldc;
     int vec;
-    __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 v, int64_t M,
-                                               int64_t N) const
+    using ColData = Staged4<T>;  // b1^(r)[col .. col+3], zero past N or without a bias
+    using ElemData = NoData;
+    static constexpr bool kColData = true, kElemData = false;
+    __device__ __forceinline__ ColData col_load(int64_t col, int64_t N) const
+    {
+        const int64_t left = N - col;
+        const int n = left <= 0 ? 0 : (left < 4 ? (int)left : 4);
+        // The bias row is contiguous: a whole group of four is one aligned vector load
+        // whenever the caller's pointer is 16-byte aligned, which the library requires.
+        return (bias && n) ? ColData::load(bias + col, n, true) : ColData::load(bias, 0, false);
+    }
+    __device__ __forceinline__ ElemData elem_load(int64_t, int64_t, int64_t, int64_t) const
+    {
+        return {};
+    }
+    __device__ __forceinline__ void apply(int64_t row, int64_t col, f32x4 v, ColData b, ElemData,
+                                          int64_t M, int64_t N) const
     {
         const int n = valid4(row, col, M, N);
         if (!n) return;
-        if (bias) v += load4(bias + col, n, true);
+        v += b.get();
         if (Z) store4(Z + row * ldc + col, v, n, vec);
         f32x4 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = act_fwd<ACT>(v[e]);
         store4(H + row * ldc + col, h, n, vec);
+    }
+    __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 v, int64_t M,
+                                               int64_t N) const
+    {
+        apply(row, col, v, col_load(col, N), {}, M, N);
     }
 };
 
@@ -113,16 +196,31 @@ struct EpiActGrad {
     T* dZ;       // [M, N]
     int64_t ldc;
     int vec;
-    __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 v, int64_t M,
-                                               int64_t N) const
+    using ColData = NoData;
+    using ElemData = Staged4<T>;  // Z[row, col .. col+3], zero outside the matrix
+    static constexpr bool kColData = false, kElemData = true;
+    __device__ __forceinline__ ColData col_load(int64_t, int64_t) const { return {}; }
+    __device__ __forceinline__ ElemData elem_load(int64_t row, int64_t col, int64_t M,
+                                                  int64_t N) const
+    {
+        const int n = valid4(row, col, M, N);
+        return n ? ElemData::load(Z + row * ldc + col, n, vec) : ElemData::load(Z, 0, false);
+    }
+    __device__ __forceinline__ void apply(int64_t row, int64_t col, f32x4 v, ColData, ElemData z,
+                                          int64_t M, int64_t N) const
     {
         const int n = valid4(row, col, M, N);
         if (!n) return;
-        const f32x4 z = load4(Z + row * ldc + col, n, vec);
+        const f32x4 zv = z.get();
         f32x4 d;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = v[e] * act_grad<ACT>(z[e]);
+        for (int e = 0; e < 4; ++e) d[e] = v[e] * act_grad<ACT>(zv[e]);
         store4(dZ + row * ldc + col, d, n, vec);
+    }
+    __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 v, int64_t M,
+                                               int64_t N) const
+    {
+        apply(row, col, v, {}, elem_load(row, col, M, N), M, N);
     }
 };
 

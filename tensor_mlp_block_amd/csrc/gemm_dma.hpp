@@ -6,10 +6,8 @@
 // K, and the m/n extent of an m/n-contiguous operand are multiples of 8.
 //
 // How the operands reach the matrix cores:
-//   * Global -> LDS with `buffer_load_dwordx4 ... lds`: each wave instruction moves 64 x 16
-//     bytes straight into a contiguous 1 KB of LDS (lane l's 16 bytes land at offset 16 l), with
-//     no register round trip. Out-of-range lanes get an offset past the buffer's range, and the
-//     hardware range check writes zeros for them, so ragged tiles need no branches.
+//   * Global -> LDS with `buffer_load_dwordx4 ... lds` (lds_dma.hpp): 1 KB per wave
+//     instruction, no register round trip, zeros for out-of-range lanes.
 //   * A k-contiguous operand is stored [rows][64 k] (128 bytes per row); an m/n-contiguous one
 //     keeps its global orientation, [64 k][rows]. In both, 16-byte chunks are XOR-swizzled with
 //     bits of the row (k) index; the swizzle is applied on the global side by choosing which
@@ -22,33 +20,9 @@
 //     and one barrier end each stage.
 #pragma once
 
-#include "common.hpp"
+#include "lds_dma.hpp"
 
 namespace mlptp {
-
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-#define MLPTP_LDS __attribute__((address_space(3)))
-
-extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4 rsrc, MLPTP_LDS uint32_t* lds,
-                                                           int size, int voffset, int soffset,
-                                                           int offset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.lds");
-
-// Buffer resource over [base, base + 2 GiB): offsets >= 0x80000000 are out of range and load
-// zeros. Word 3 is the gfx9-family default (32-bit dword format, no swizzle).
-__device__ __forceinline__ i32x4 make_buffer_rsrc(const void* base)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    i32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a & 0xffffffffu));
-    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xffffu));
-    r[2] = (int)0x80000000u;
-    r[3] = 0x00020000;
-    return r;
-}
-
-constexpr int kOutOfRange = (int)0x80000000u;
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int GROUP_M_ = 4>
 struct DmaTile {
@@ -157,25 +131,8 @@ __device__ __forceinline__ bf16x8 frag_mc(const MLPTP_LDS uint8_t* lds, int row0
         h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             reinterpret_cast<MLPTP_LDS s16x4*>(const_cast<MLPTP_LDS uint8_t*>(p)));
     }
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
     s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
     return __builtin_bit_cast(bf16x8, v);
-}
-
-template <int GROUP_M>
-__device__ __forceinline__ void dma_tile_coords(int64_t bid, int64_t tiles_m, int64_t tiles_n,
-                                                int64_t& tm, int64_t& tn)
-{
-    const int64_t ntiles = tiles_m * tiles_n;
-    constexpr int kXcds = 8;
-    if (ntiles % kXcds == 0) bid = (bid % kXcds) * (ntiles / kXcds) + bid / kXcds;
-    const int64_t per_group = (int64_t)GROUP_M * tiles_n;
-    const int64_t group = bid / per_group;
-    const int64_t first_m = group * GROUP_M;
-    const int64_t gm = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
-    const int64_t in_group = bid % per_group;
-    tm = first_m + in_group % gm;
-    tn = in_group / gm;
 }
 
 struct DmaCtx {
@@ -245,7 +202,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void gemm_bf16_dma(
 
     const int64_t tiles_m = ceil_div(M, Cfg::BM), tiles_n = ceil_div(N, Cfg::BN);
     int64_t tm, tn;
-    dma_tile_coords<Cfg::GROUP_M>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    tile_coords<Cfg::GROUP_M>(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
     const int m_left = (int)((M - m0) < Cfg::BM ? (M - m0) : Cfg::BM);
     const int n_left = (int)((N - n0) < Cfg::BN ? (N - n0) : Cfg::BN);
@@ -255,6 +212,16 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void gemm_bf16_dma(
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
         for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Per-column epilogue data (the bias) is fetched before the main loop, so its latency hides
+    // under the MFMAs instead of stalling the epilogue between stores.
+    const int frow = lane & 15, fchunk = lane >> 4;
+    typename Epi::ColData cdat[Cfg::FN];
+    if constexpr (Epi::kColData) {
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+            cdat[j] = epi.col_load(n0 + wn * Cfg::WTN + j * 16 + 4 * fchunk, N);
+    }
 
     const int64_t nk = ceil_div(K, Cfg::BK);
     const DmaCtx ctx{A, B, M, N, K, lda, ldb, m0, n0, m_left, n_left, wave, lane};
@@ -271,14 +238,16 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void gemm_bf16_dma(
         __syncthreads();
     }
 
-    const int frow = lane & 15, fchunk = lane >> 4;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
         const int64_t row = m0 + wm * Cfg::WTM + i * 16 + frow;
 #pragma unroll
         for (int j = 0; j < Cfg::FN; ++j) {
             const int64_t col = n0 + wn * Cfg::WTN + j * 16 + 4 * fchunk;
-            epi(row, col, acc[i][j], M, N);
+            if constexpr (Epi::kColData)
+                epi.apply(row, col, acc[i][j], cdat[j], {}, M, N);
+            else
+                epi(row, col, acc[i][j], M, N);
         }
     }
 }

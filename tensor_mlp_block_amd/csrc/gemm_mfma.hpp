@@ -33,6 +33,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "lds_dma.hpp"
 
 namespace mlptp {
 
@@ -149,24 +150,6 @@ struct TileLoader {
         }
     }
 };
-
-// Maps the linear workgroup index to a (tile_m, tile_n) pair: XCD-contiguous ranges, then
-// GROUP_M-row grouped order inside the range. A bijection on [0, tiles_m * tiles_n).
-template <int GROUP_M>
-__device__ __forceinline__ void tile_coords(int64_t bid, int64_t tiles_m, int64_t tiles_n,
-                                            int64_t& tm, int64_t& tn)
-{
-    const int64_t ntiles = tiles_m * tiles_n;
-    constexpr int kXcds = 8;
-    if (ntiles % kXcds == 0) bid = (bid % kXcds) * (ntiles / kXcds) + bid / kXcds;
-    const int64_t per_group = (int64_t)GROUP_M * tiles_n;
-    const int64_t group = bid / per_group;
-    const int64_t first_m = group * GROUP_M;
-    const int64_t gm = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
-    const int64_t in_group = bid % per_group;
-    tm = first_m + in_group % gm;
-    tn = in_group / gm;
-}
 
 template <class Cfg, bool A_KC, bool B_KC, class Epi>
 __global__ __launch_bounds__(Cfg::NTHREADS, 1) void gemm_bf16_mfma(
