@@ -5,7 +5,7 @@ CPU-baseline leg, never by the GPU library or its binding. It shares no code wit
 
 Every function takes array-likes (numpy arrays or CPU torch tensors of any float dtype),
 widens them to contiguous fp64 (exact for bf16 and fp32 inputs) and returns fp64 numpy
-arrays. Shapes follow the oracle's C header comment: X [N,D], W1 [D,F], b1 [F], W2 [F,D],
+arrays. Shapes follow the oracle's C header comment: X [N,D], W1, Wg, Wu [D,F], b1 [F], W2 [F,D],
 b2 [D], dY [N,D]; shard outputs are [N, F/T] and [N, D].
 
 Parity status of each function is pinned by the tests under ``tests/test_oracle_*.py``:
@@ -47,9 +47,20 @@ def _load():
         lib.oracle_dense_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci,
                                          vp, vp, vp, vp, vp]
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_token_slice.argtypes = [i64, i32, i32, vp, vp]
+        lib.oracle_partial_reduce_scatter.argtypes = [vp, i32, i32, vp, i64, i64, vp]
+        lib.oracle_silu_vec.argtypes = [vp, vp, i64, ci]
+        lib.oracle_swiglu_shard_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32,
+                                                vp, vp, vp, vp]
+        lib.oracle_swiglu_dense_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+        lib.oracle_swiglu_shard_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
+                                                vp, vp, vp, vp, vp, vp]
         for name in ("oracle_act_vec", "oracle_act_deriv_vec", "oracle_shard_fwd",
                      "oracle_partial_sum", "oracle_block_fwd", "oracle_dense_fwd",
-                     "oracle_shard_bwd", "oracle_dense_bwd", "oracle_num_threads"):
+                     "oracle_shard_bwd", "oracle_dense_bwd", "oracle_num_threads",
+                     "oracle_token_slice", "oracle_partial_reduce_scatter", "oracle_silu_vec",
+                     "oracle_swiglu_shard_fwd", "oracle_swiglu_dense_fwd",
+                     "oracle_swiglu_shard_bwd"):
             getattr(lib, name).restype = ci
         _lib = lib
     return _lib
@@ -181,6 +192,90 @@ def dense_bwd(X, W1, b1, W2, dY, act="gelu_tanh"):
                                     _act_code(act), _p(out["dW1"]), _p(out["db1"]),
                                     _p(out["dW2"]), _p(out["db2"]), _p(out["dX"])),
            "oracle_dense_bwd")
+    return out
+
+
+def token_slice(N, T, r):
+    """(first row, row count) of token slice r of T in the reduce-scatter layout."""
+    row0, rows = ctypes.c_int64(), ctypes.c_int64()
+    _check(_load().oracle_token_slice(N, T, r, ctypes.byref(row0), ctypes.byref(rows)),
+           "oracle_token_slice")
+    return row0.value, rows.value
+
+
+def partial_reduce_scatter(partials, r, b2=None):
+    """Token slice r of ((P0 + P1) + ...) + b2: the rows token_slice(N, T, r) of the tail."""
+    Ps = [_f64(p) for p in partials]
+    T = len(Ps)
+    N, D = Ps[0].shape
+    for p in Ps:
+        if p.shape != (N, D):
+            raise OracleError("partials differ in shape")
+    b2 = _f64(b2)
+    arr = (ctypes.c_void_p * T)(*[p.ctypes.data for p in Ps])
+    _, rows = token_slice(N, T, r) if 0 <= r < T else (0, 0)
+    Yr = np.empty((rows, D))
+    _check(_load().oracle_partial_reduce_scatter(ctypes.cast(arr, ctypes.c_void_p), T, r,
+                                                 _p(b2), N, D, _p(Yr)),
+           "oracle_partial_reduce_scatter")
+    return Yr
+
+
+def silu(z):
+    z = _f64(z)
+    out = np.empty_like(z)
+    _check(_load().oracle_silu_vec(_p(z), _p(out), z.size, 0), "oracle_silu_vec")
+    return out
+
+
+def silu_deriv(z):
+    z = _f64(z)
+    out = np.empty_like(z)
+    _check(_load().oracle_silu_vec(_p(z), _p(out), z.size, 1), "oracle_silu_vec")
+    return out
+
+
+def _gated_dims(X, Wg, Wu, W2):
+    N, D = X.shape
+    D1, F = Wg.shape
+    if D1 != D or Wu.shape != (D, F) or W2.shape != (F, D):
+        raise OracleError(f"shape mismatch X{X.shape} Wg{Wg.shape} Wu{Wu.shape} W2{W2.shape}")
+    return N, D, F
+
+
+def swiglu_shard_fwd(X, Wg, Wu, W2, T, r):
+    """(G, U, H, P) of gated shard r of T; Wg, Wu, W2 are the full weights."""
+    X, Wg, Wu, W2 = _f64(X), _f64(Wg), _f64(Wu), _f64(W2)
+    N, D, F = _gated_dims(X, Wg, Wu, W2)
+    fs = F // T if T > 0 else 0
+    G = np.empty((N, fs)); U = np.empty((N, fs)); H = np.empty((N, fs)); P = np.empty((N, D))
+    _check(_load().oracle_swiglu_shard_fwd(_p(X), _p(Wg), _p(Wu), _p(W2), N, D, F, T, r,
+                                           _p(G), _p(U), _p(H), _p(P)),
+           "oracle_swiglu_shard_fwd")
+    return G, U, H, P
+
+
+def swiglu_dense_fwd(X, Wg, Wu, W2):
+    X, Wg, Wu, W2 = _f64(X), _f64(Wg), _f64(Wu), _f64(W2)
+    N, D, F = _gated_dims(X, Wg, Wu, W2)
+    Y = np.empty((N, D))
+    _check(_load().oracle_swiglu_dense_fwd(_p(X), _p(Wg), _p(Wu), _p(W2), N, D, F, _p(Y)),
+           "oracle_swiglu_dense_fwd")
+    return Y
+
+
+def swiglu_shard_bwd(X, Wg, Wu, W2, dY, T, r):
+    """Gradients of gated shard r: dict with dG, dU [N,Fs], dWg, dWu [D,Fs], dW2 [Fs,D],
+    dX [N,D]."""
+    X, Wg, Wu, W2, dY = _f64(X), _f64(Wg), _f64(Wu), _f64(W2), _f64(dY)
+    N, D, F = _gated_dims(X, Wg, Wu, W2)
+    fs = F // T if T > 0 else 0
+    out = {"dG": np.empty((N, fs)), "dU": np.empty((N, fs)), "dWg": np.empty((D, fs)),
+           "dWu": np.empty((D, fs)), "dW2": np.empty((fs, D)), "dX": np.empty((N, D))}
+    _check(_load().oracle_swiglu_shard_bwd(_p(X), _p(Wg), _p(Wu), _p(W2), _p(dY), N, D, F, T,
+                                           r, _p(out["dG"]), _p(out["dU"]), _p(out["dWg"]),
+                                           _p(out["dWu"]), _p(out["dW2"]), _p(out["dX"])),
+           "oracle_swiglu_shard_bwd")
     return out
 
 

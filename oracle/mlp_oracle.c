@@ -32,9 +32,13 @@
  *     and Gimpel (2016), and the sigmoid form.
  *   - ReLU'(0) = 0: the gradient passes only where Z > 0.
  *   - b1 is added before the activation; b2 is added once, after the sum over shards.
+ *   - SiLU, named by the gated form without a formula, is z * sigmoid(z) = z / (1 + exp(-z));
+ *     the gated form as the page writes it has no biases.
+ *   - The token slices of the reduce-scatter layout are contiguous and as equal as possible,
+ *     the first ones full: S = ceil(N / T) rows each, the last ones shorter or empty.
  *
- * Layout: every array is fp64, row-major and contiguous. X [N,D]; W1 [D,F]; b1 [F];
- * W2 [F,D]; b2 [D]; Z, H, dZ [N,Fs]; P, Y, dX [N,D]; dW1 [D,Fs]; db1 [Fs]; dW2 [Fs,D].
+ * Layout: every array is fp64, row-major and contiguous. X [N,D]; W1, Wg, Wu [D,F]; b1 [F];
+ * W2 [F,D]; b2 [D]; Z, G, U, H, dZ [N,Fs]; P, Y, dX [N,D]; dW1 [D,Fs]; db1 [Fs]; dW2 [Fs,D].
  * Each output element accumulates its reduction index in ascending order. OpenMP only
  * splits independent output rows (or columns) across threads; no element's arithmetic
  * changes with the thread count.
@@ -398,6 +402,215 @@ int oracle_dense_bwd(const double* X, const double* W1, const double* b1, const 
         for (int64_t n = 0; n < N; ++n)
             for (int64_t d = 0; d < D; ++d) db2[d] += dY[n * D + d];
     }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* Reduce-scatter layout of the block tail [Z 04].                                           */
+
+/* First row and row count of token slice r: S = ceil(N / T) rows per slice. */
+int oracle_token_slice(int64_t N, int32_t T, int32_t r, int64_t* row0, int64_t* rows)
+{
+    if (N < 0 || T < 1 || r < 0 || r >= T) return -2;
+    if (!row0 || !rows) return -1;
+    int64_t S = (N + T - 1) / T;
+    int64_t a = (int64_t)r * S, b = a + S;
+    if (a > N) a = N;
+    if (b > N) b = N;
+    *row0 = a;
+    *rows = b - a;
+    return 0;
+}
+
+/*
+ * Token slice r of the block tail: Yr[i,d] = (sum_s P^(s)[row0 + i, d]) + b2[d] for the rows of
+ * slice r, shards summed in rank order, b2 added once [Z 04], [Z 05]. Yr is [rows, D].
+ */
+int oracle_partial_reduce_scatter(const double* const* P, int32_t T, int32_t r,
+                                  const double* b2, int64_t N, int64_t D, double* Yr)
+{
+    if (N <= 0 || D <= 0 || T < 1 || r < 0 || r >= T) return -2;
+    if (!P || !Yr) return -1;
+    for (int32_t s = 0; s < T; ++s)
+        if (!P[s]) return -1;
+    int64_t row0, rows;
+    oracle_token_slice(N, T, r, &row0, &rows);
+    for (int64_t i = 0; i < rows; ++i) {
+        int64_t n = row0 + i;
+        for (int64_t d = 0; d < D; ++d) {
+            double v = P[0][n * D + d];
+            for (int32_t s = 1; s < T; ++s) v += P[s][n * D + d];
+            if (b2) v += b2[d];
+            Yr[i * D + d] = v;
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* Gated (SwiGLU) MLP [Z 08].                                                                */
+
+/* SiLU(z) = z * sigmoid(z). */
+double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z), by the product rule. */
+double oracle_silu_deriv(double z)
+{
+    double s = 1.0 / (1.0 + exp(-z));
+    return s * (1.0 + z * (1.0 - s));
+}
+
+int oracle_silu_vec(const double* z, double* out, int64_t n, int deriv)
+{
+    if (!z || !out) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = deriv ? oracle_silu_deriv(z[i]) : oracle_silu(z[i]);
+    return 0;
+}
+
+/* A[n,j] = sum_k X[n,k] W[k, c0 + j], k ascending: one column slice of a [D,F] weight. */
+static void column_slice_product(const double* X, const double* W, int64_t N, int64_t D,
+                                 int64_t F, int64_t Fs, int64_t c0, double* A)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double* a = A + n * Fs;
+        for (int64_t j = 0; j < Fs; ++j) a[j] = 0.0;
+        for (int64_t k = 0; k < D; ++k) {
+            double x = X[n * D + k];
+            const double* w = W + k * F + c0;
+            for (int64_t j = 0; j < Fs; ++j) a[j] += x * w[j];
+        }
+    }
+}
+
+/*
+ * One rank's gated shard: gate and up projections with the SAME column slice of Wg and Wu,
+ * H = SiLU(G) (.) U locally, then the row slice of W2 to a full-shape partial [Z 08]. Wg, Wu,
+ * W2 are the FULL weights. G, U may be NULL; H [N,Fs] and P [N,D] are required.
+ */
+int oracle_swiglu_shard_fwd(const double* X, const double* Wg, const double* Wu,
+                            const double* W2, int64_t N, int64_t D, int64_t F, int32_t T,
+                            int32_t r, double* G, double* U, double* H, double* P)
+{
+    int rc = check_shard_args(N, D, F, T, r, 0);
+    if (rc) return rc;
+    if (!X || !Wg || !Wu || !W2 || !H || !P) return -1;
+    int64_t Fs = F / T, c0 = (int64_t)r * Fs;
+    double* g = G ? G : (double*)malloc((size_t)(N * Fs) * sizeof(double));
+    double* u = U ? U : (double*)malloc((size_t)(N * Fs) * sizeof(double));
+    if (!g || !u) {
+        if (!G) free(g);
+        if (!U) free(u);
+        return -1;
+    }
+    column_slice_product(X, Wg, N, D, F, Fs, c0, g);
+    column_slice_product(X, Wu, N, D, F, Fs, c0, u);
+    for (int64_t i = 0; i < N * Fs; ++i) H[i] = oracle_silu(g[i]) * u[i];
+    down_projection(H, W2, N, D, Fs, c0, P);
+    if (!G) free(g);
+    if (!U) free(u);
+    return 0;
+}
+
+/* The unsharded gated MLP: Y = (SiLU(X Wg) (.) (X Wu)) W2 [Z 08]. */
+int oracle_swiglu_dense_fwd(const double* X, const double* Wg, const double* Wu,
+                            const double* W2, int64_t N, int64_t D, int64_t F, double* Y)
+{
+    int rc = check_shard_args(N, D, F, 1, 0, 0);
+    if (rc) return rc;
+    if (!X || !Wg || !Wu || !W2 || !Y) return -1;
+    double* H = (double*)malloc((size_t)(N * F) * sizeof(double));
+    if (!H) return -1;
+    rc = oracle_swiglu_shard_fwd(X, Wg, Wu, W2, N, D, F, 1, 0, NULL, NULL, H, Y);
+    free(H);
+    return rc;
+}
+
+/*
+ * Backward of the gated shard r for dY [N,D]. Recomputes G, U and H in fp64. Outputs (any
+ * may be NULL except dG and dU): dG, dU [N,Fs]; dWg, dWu [D,Fs]; dW2r [Fs,D]; dXr [N,D].
+ */
+int oracle_swiglu_shard_bwd(const double* X, const double* Wg, const double* Wu,
+                            const double* W2, const double* dY, int64_t N, int64_t D, int64_t F,
+                            int32_t T, int32_t r, double* dG, double* dU, double* dWg,
+                            double* dWu, double* dW2r, double* dXr)
+{
+    int rc = check_shard_args(N, D, F, T, r, 0);
+    if (rc) return rc;
+    if (!X || !Wg || !Wu || !W2 || !dY || !dG || !dU) return -1;
+    int64_t Fs = F / T, c0 = (int64_t)r * Fs;
+    double* G = (double*)malloc((size_t)(N * Fs) * sizeof(double));
+    double* U = (double*)malloc((size_t)(N * Fs) * sizeof(double));
+    double* H = (double*)malloc((size_t)(N * Fs) * sizeof(double));
+    if (!G || !U || !H) {
+        free(G);
+        free(U);
+        free(H);
+        return -1;
+    }
+    column_slice_product(X, Wg, N, D, F, Fs, c0, G);
+    column_slice_product(X, Wu, N, D, F, Fs, c0, U);
+    for (int64_t i = 0; i < N * Fs; ++i) H[i] = oracle_silu(G[i]) * U[i];
+
+    /* dH[n,j] = sum_d dY[n,d] W2[c0+j, d]; then the product rule through H = SiLU(G) U. */
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < Fs; ++j) {
+            const double* w = W2 + (c0 + j) * D;
+            double s = 0.0;
+            for (int64_t d = 0; d < D; ++d) s += dY[n * D + d] * w[d];
+            double g = G[n * Fs + j], u = U[n * Fs + j];
+            dG[n * Fs + j] = s * u * oracle_silu_deriv(g);
+            dU[n * Fs + j] = s * oracle_silu(g);
+        }
+    }
+
+    /* dW2r[j,d] = sum_n H[n,j] dY[n,d]. */
+    if (dW2r) {
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < Fs; ++j) {
+            double* g = dW2r + j * D;
+            for (int64_t d = 0; d < D; ++d) g[d] = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double h = H[n * Fs + j];
+                for (int64_t d = 0; d < D; ++d) g[d] += h * dY[n * D + d];
+            }
+        }
+    }
+
+    /* dWg[k,j] = sum_n X[n,k] dG[n,j];  dWu[k,j] = sum_n X[n,k] dU[n,j]. */
+    for (int pass = 0; pass < 2; ++pass) {
+        double* out = pass == 0 ? dWg : dWu;
+        const double* dA = pass == 0 ? dG : dU;
+        if (!out) continue;
+#pragma omp parallel for schedule(static)
+        for (int64_t k = 0; k < D; ++k) {
+            double* g = out + k * Fs;
+            for (int64_t j = 0; j < Fs; ++j) g[j] = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double x = X[n * D + k];
+                for (int64_t j = 0; j < Fs; ++j) g[j] += x * dA[n * Fs + j];
+            }
+        }
+    }
+
+    /* dXr[n,k] = sum_j dG[n,j] Wg[k,c0+j] + sum_j dU[n,j] Wu[k,c0+j]. */
+    if (dXr) {
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < D; ++k) {
+                const double* wg = Wg + k * F + c0;
+                const double* wu = Wu + k * F + c0;
+                double s = 0.0;
+                for (int64_t j = 0; j < Fs; ++j) s += dG[n * Fs + j] * wg[j];
+                for (int64_t j = 0; j < Fs; ++j) s += dU[n * Fs + j] * wu[j];
+                dXr[n * D + k] = s;
+            }
+        }
+    }
+    free(G);
+    free(U);
+    free(H);
     return 0;
 }
 
