@@ -130,6 +130,73 @@ int mlp_tp_partial_reduce(const float* const* P, int32_t T, const void* b2, int3
                           float* Y, int64_t N, int64_t D, void* stream);
 
 /*
+ * Rows of token slice r in the reduce-scatter layout of the block tail [Z 04]: slices are
+ * contiguous, S = ceil(N / T) rows each in rank order, the last ones shorter or empty.
+ *   row0, rows  HOST pointers receiving the first row and the row count of slice r.
+ * Errors: E_NULL (row0, rows), E_SHAPE (N < 0, T < 1, r outside [0, T)). Launches nothing.
+ */
+int mlp_tp_token_slice(int64_t N, int32_t T, int32_t r, int64_t* row0, int64_t* rows);
+
+/*
+ * Block-tail reduction in the reduce-scatter layout [Z 04], [Z 05]: only token slice r of
+ *     Y = (((P[0] + P[1]) + ...) + P[T-1]) + b2
+ * is formed, so the residual stream stays token-sharded. It is the share of the sum that the
+ * reduce-scatter of the row-parallel output leaves on rank r, computed here over T partials
+ * resident in this GPU's memory; b2 is added once, to that rank's rows only.
+ *   P   HOST array of T device pointers, each to a float [N, D] partial (whole partials).
+ *   r   the slice, 0 <= r < T; its rows are those mlp_tp_token_slice(N, T, r) returns.
+ *   b2  [D] of b2_dtype; NULL means no bias.
+ *   Yr  [rows, D] float output. Yr may be exactly equal to P[s] + row0 * D for any s (in place
+ *       over that partial's own slice rows); any other overlap with a partial or b2 is E_ALIAS.
+ *       When the slice is empty Yr is not touched and may be NULL.
+ * Errors: as mlp_tp_partial_reduce, and E_SHAPE for r outside [0, T). An empty slice is a no-op.
+ */
+int mlp_tp_partial_reduce_scatter(const float* const* P, int32_t T, int32_t r, const void* b2,
+                                  int32_t b2_dtype, float* Yr, int64_t N, int64_t D, void* stream);
+
+/*
+ * Row-parallel down-projection added into a running fp32 sum [Z 02]:
+ *     P += H . W2r
+ * The one-GPU, one-buffer form of the block tail: the T shards, computed in turn, add their
+ * partials into P (which the caller zeroes or seeds first), so no T separate [N, D] partials
+ * are kept. Shapes, dtypes and errors as mlp_tp_down_proj. Calls on one P must be ordered on
+ * one stream; the fp32 sum then follows rank order exactly like mlp_tp_partial_reduce.
+ */
+int mlp_tp_down_proj_accumulate(const void* H, const void* W2r, float* P, int64_t N, int64_t D,
+                                int64_t F, int32_t T, int32_t dtype, void* stream);
+
+/*
+ * Gated (SwiGLU) up-projection [Z 08]: the gate and up projections are cut at the SAME columns,
+ * so each rank multiplies matching channels locally:
+ *     G = X . Wgr,   U = X . Wur   (fp32 accumulate),   H = SiLU(G) * U,   SiLU(z) = z sigmoid(z).
+ *   X    [N, D]   dtype, replicated input.
+ *   Wgr  [D, Fs]  dtype, the gate weight's column slice Wg[:, r*Fs:(r+1)*Fs].
+ *   Wur  [D, Fs]  dtype, the up weight's slice over the same columns.
+ *   G, U [N, Fs]  dtype outputs, the two projections kept for a backward; NULL skips each.
+ *   H    [N, Fs]  dtype output.
+ * As on the page, the gated form has no biases. In bf16, G and U are rounded once when stored.
+ * When D and Fs are multiples of 8 (bf16), the gate and up products share one GEMM pass and H
+ * is formed from their fp32 values; otherwise the gate is computed first, rounded to dtype,
+ * and H is formed from that rounded gate.
+ * Errors: E_NULL (X, Wgr, Wur, H), E_SHAPE, E_INDIVISIBLE, E_DTYPE, E_ALIGN, E_ALIAS (H, G or U
+ * overlapping X, Wgr, Wur or each other), E_HIP.
+ */
+int mlp_tp_swiglu_up_proj(const void* X, const void* Wgr, const void* Wur, void* G, void* U,
+                          void* H, int64_t N, int64_t D, int64_t F, int32_t T, int32_t dtype,
+                          void* stream);
+
+/*
+ * One rank's gated forward shard: mlp_tp_swiglu_up_proj then mlp_tp_down_proj on one stream
+ * [Z 08]. No b2, as for mlp_tp_shard_fwd.
+ *   X [N, D], Wgr, Wur [D, Fs], W2r [Fs, D]: dtype inputs.
+ *   G, U [N, Fs] dtype outputs (nullable); H [N, Fs] dtype output; P [N, D] float output.
+ * Errors: those of the two calls; all arguments are checked before the first launch.
+ */
+int mlp_tp_swiglu_shard_fwd(const void* X, const void* Wgr, const void* Wur, const void* W2r,
+                            void* G, void* U, void* H, float* P, int64_t N, int64_t D, int64_t F,
+                            int32_t T, int32_t dtype, void* stream);
+
+/*
  * Bytes of device workspace mlp_tp_shard_bwd needs for these sizes (0 if none); a negative
  * MLP_TP_E_* code for invalid sizes.
  */

@@ -53,6 +53,14 @@ def load() -> ctypes.CDLL:
         "mlp_tp_shard_bwd_workspace_bytes": ([i64, i64, i64, i32], ctypes.c_int64),
         "mlp_tp_shard_bwd": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                               i64, i64, i64, i32, i32, i32, vp], ctypes.c_int),
+        "mlp_tp_token_slice": ([i64, i32, i32, vp, vp], ctypes.c_int),
+        "mlp_tp_partial_reduce_scatter": ([vp, i32, i32, vp, i32, vp, i64, i64, vp],
+                                          ctypes.c_int),
+        "mlp_tp_down_proj_accumulate": ([vp, vp, vp, i64, i64, i64, i32, i32, vp], ctypes.c_int),
+        "mlp_tp_swiglu_up_proj": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp],
+                                  ctypes.c_int),
+        "mlp_tp_swiglu_shard_fwd": ([vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
+                                     vp], ctypes.c_int),
         "mlp_tp_strerror": ([ctypes.c_int], ctypes.c_char_p),
     }
     for name, (args, res) in sigs.items():
@@ -126,6 +134,42 @@ def mlp_tp_partial_reduce(P, T, b2, b2_dtype, Y, N, D, stream=None):
     rc = load().mlp_tp_partial_reduce(ctypes.cast(ptrs, ctypes.c_void_p), T, _ptr(b2), b2_dtype,
                                       _ptr(Y), N, D, _stream(stream))
     return _check(rc, "mlp_tp_partial_reduce")
+
+
+def mlp_tp_token_slice(N, T, r):
+    """(first row, row count) of token slice r in the reduce-scatter layout."""
+    row0, rows = ctypes.c_int64(), ctypes.c_int64()
+    rc = load().mlp_tp_token_slice(N, T, r, ctypes.cast(ctypes.byref(row0), ctypes.c_void_p),
+                                   ctypes.cast(ctypes.byref(rows), ctypes.c_void_p))
+    _check(rc, "mlp_tp_token_slice")
+    return row0.value, rows.value
+
+
+def mlp_tp_partial_reduce_scatter(P, T, r, b2, b2_dtype, Yr, N, D, stream=None):
+    """Token slice r of the block tail into Yr [rows, D]; P as for mlp_tp_partial_reduce."""
+    ptrs = (ctypes.c_void_p * max(1, len(P)))(*[_ptr(p) for p in P])
+    rc = load().mlp_tp_partial_reduce_scatter(ctypes.cast(ptrs, ctypes.c_void_p), T, r, _ptr(b2),
+                                              b2_dtype, _ptr(Yr), N, D, _stream(stream))
+    return _check(rc, "mlp_tp_partial_reduce_scatter")
+
+
+def mlp_tp_down_proj_accumulate(H, W2r, P, N, D, F, T, dtype, stream=None):
+    rc = load().mlp_tp_down_proj_accumulate(_ptr(H), _ptr(W2r), _ptr(P), N, D, F, T, dtype,
+                                            _stream(stream))
+    return _check(rc, "mlp_tp_down_proj_accumulate")
+
+
+def mlp_tp_swiglu_up_proj(X, Wgr, Wur, G, U, H, N, D, F, T, dtype, stream=None):
+    rc = load().mlp_tp_swiglu_up_proj(_ptr(X), _ptr(Wgr), _ptr(Wur), _ptr(G), _ptr(U), _ptr(H),
+                                      N, D, F, T, dtype, _stream(stream))
+    return _check(rc, "mlp_tp_swiglu_up_proj")
+
+
+def mlp_tp_swiglu_shard_fwd(X, Wgr, Wur, W2r, G, U, H, P, N, D, F, T, dtype, stream=None):
+    rc = load().mlp_tp_swiglu_shard_fwd(_ptr(X), _ptr(Wgr), _ptr(Wur), _ptr(W2r), _ptr(G),
+                                        _ptr(U), _ptr(H), _ptr(P), N, D, F, T, dtype,
+                                        _stream(stream))
+    return _check(rc, "mlp_tp_swiglu_shard_fwd")
 
 
 def mlp_tp_shard_bwd_workspace_bytes(N, D, F, T) -> int:

@@ -103,6 +103,45 @@ int check_down(const void* H, const void* W2r, const float* P, int64_t N, int64_
     return disjoint({{P, N * D * 4}}, {{H, N * Fs * es}, {W2r, Fs * D * es}});
 }
 
+int check_swiglu_up(const void* X, const void* Wg, const void* Wu, void* G, void* U, void* H,
+                    int64_t N, int64_t D, int64_t F, int32_t T, int32_t dtype)
+{
+    if (!X || !Wg || !Wu || !H) return MLP_TP_E_NULL;
+    if (int rc = check_shard_shape(N, D, F, T)) return rc;
+    if (!dtype_ok(dtype)) return MLP_TP_E_DTYPE;
+    if (int rc = all_aligned({X, Wg, Wu, G, U, H})) return rc;
+    const int64_t es = elem_size(dtype), Fs = F / T;
+    return disjoint({{H, N * Fs * es}, {G, N * Fs * es}, {U, N * Fs * es}},
+                    {{X, N * D * es}, {Wg, D * Fs * es}, {Wu, D * Fs * es}});
+}
+
+// The reduce's own checks (shared by the full and the token-slice forms), except aliasing.
+// Y may be NULL only where the caller allows it (an empty token slice).
+int check_reduce(const float* const* P, int32_t T, const void* b2, int32_t b2_dtype,
+                 const float* Y, int64_t N, int64_t D, bool y_optional = false)
+{
+    if (!P || (!Y && !y_optional)) return MLP_TP_E_NULL;
+    if (T < 1 || T > MLP_TP_MAX_REDUCE_T || N < 0 || D <= 0 || N > kMaxDim || D > kMaxDim ||
+        N * D > kMaxElems)
+        return MLP_TP_E_SHAPE;
+    for (int32_t r = 0; r < T; ++r)
+        if (!P[r]) return MLP_TP_E_NULL;
+    if (b2 && !dtype_ok(b2_dtype)) return MLP_TP_E_DTYPE;
+    if ((Y && !aligned16(Y)) || (b2 && !aligned16(b2))) return MLP_TP_E_ALIGN;
+    for (int32_t r = 0; r < T; ++r)
+        if (!aligned16(P[r])) return MLP_TP_E_ALIGN;
+    return MLP_TP_OK;
+}
+
+// Token slice r of N rows over T ranks: S = ceil(N / T) rows per slice [Z 04].
+void token_slice(int64_t N, int32_t T, int32_t r, int64_t& row0, int64_t& rows)
+{
+    const int64_t S = (N + T - 1) / T;
+    int64_t a = (int64_t)r * S, b = a + S;
+    row0 = a < N ? a : N;
+    rows = (b < N ? b : N) - row0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -152,22 +191,89 @@ int mlp_tp_shard_fwd(const void* X, const void* W1r, const void* b1r, const void
 int mlp_tp_partial_reduce(const float* const* P, int32_t T, const void* b2, int32_t b2_dtype,
                           float* Y, int64_t N, int64_t D, void* stream)
 {
-    if (!P || !Y) return MLP_TP_E_NULL;
-    if (T < 1 || T > MLP_TP_MAX_REDUCE_T || N < 0 || D <= 0 || N > kMaxDim || D > kMaxDim ||
-        N * D > kMaxElems)
-        return MLP_TP_E_SHAPE;
-    for (int32_t r = 0; r < T; ++r)
-        if (!P[r]) return MLP_TP_E_NULL;
-    if (b2 && !dtype_ok(b2_dtype)) return MLP_TP_E_DTYPE;
-    if (!aligned16(Y) || (b2 && !aligned16(b2))) return MLP_TP_E_ALIGN;
-    for (int32_t r = 0; r < T; ++r)
-        if (!aligned16(P[r])) return MLP_TP_E_ALIGN;
+    if (int rc = check_reduce(P, T, b2, b2_dtype, Y, N, D)) return rc;
     const int64_t bytes = N * D * 4;
     for (int32_t r = 0; r < T; ++r)
         if (P[r] != Y && overlap({Y, bytes}, {P[r], bytes})) return MLP_TP_E_ALIAS;
     if (b2 && overlap({Y, bytes}, {b2, D * elem_size(b2_dtype)})) return MLP_TP_E_ALIAS;
     if (N == 0) return MLP_TP_OK;
     mlptp::launch_partial_reduce(P, T, b2, b2_dtype, Y, N, D, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int mlp_tp_token_slice(int64_t N, int32_t T, int32_t r, int64_t* row0, int64_t* rows)
+{
+    if (!row0 || !rows) return MLP_TP_E_NULL;
+    if (N < 0 || T < 1 || r < 0 || r >= T) return MLP_TP_E_SHAPE;
+    token_slice(N, T, r, *row0, *rows);
+    return MLP_TP_OK;
+}
+
+int mlp_tp_partial_reduce_scatter(const float* const* P, int32_t T, int32_t r, const void* b2,
+                                  int32_t b2_dtype, float* Yr, int64_t N, int64_t D, void* stream)
+{
+    // An empty slice has no rows to write: Yr may then be NULL (an empty tensor's pointer).
+    const bool slice_ok = T >= 1 && r >= 0 && r < T && N >= 0;
+    int64_t row0 = 0, rows = 0;
+    if (slice_ok) token_slice(N, T, r, row0, rows);
+    if (int rc = check_reduce(P, T, b2, b2_dtype, Yr, N, D, slice_ok && rows == 0)) return rc;
+    if (r < 0 || r >= T) return MLP_TP_E_SHAPE;
+    if (rows == 0) return MLP_TP_OK;
+    const int64_t bytes = rows * D * 4, full = N * D * 4;
+    for (int32_t s = 0; s < T; ++s)
+        if (Yr != P[s] + row0 * D && overlap({Yr, bytes}, {P[s], full})) return MLP_TP_E_ALIAS;
+    if (b2 && overlap({Yr, bytes}, {b2, D * elem_size(b2_dtype)})) return MLP_TP_E_ALIAS;
+    // The slice's rows of every partial, reduced as a [rows, D] block tail. With D % 4 == 0 the
+    // offset keeps each pointer 16-byte aligned; otherwise the reduce takes its element path.
+    const float* Ps[MLP_TP_MAX_REDUCE_T];
+    for (int32_t s = 0; s < T; ++s) Ps[s] = P[s] + row0 * D;
+    mlptp::launch_partial_reduce(Ps, T, b2, b2_dtype, Yr, rows, D,
+                                 static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int mlp_tp_down_proj_accumulate(const void* H, const void* W2r, float* P, int64_t N, int64_t D,
+                                int64_t F, int32_t T, int32_t dtype, void* stream)
+{
+    if (int rc = check_down(H, W2r, P, N, D, F, T, dtype)) return rc;
+    if (N == 0) return MLP_TP_OK;
+    mlptp::launch_down_proj_accumulate(H, W2r, P, N, D, F / T, dtype,
+                                       static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int mlp_tp_swiglu_up_proj(const void* X, const void* Wgr, const void* Wur, void* G, void* U,
+                          void* H, int64_t N, int64_t D, int64_t F, int32_t T, int32_t dtype,
+                          void* stream)
+{
+    if (int rc = check_swiglu_up(X, Wgr, Wur, G, U, H, N, D, F, T, dtype)) return rc;
+    if (N == 0) return MLP_TP_OK;
+    mlptp::launch_swiglu_up(X, Wgr, Wur, G, U, H, N, D, F / T, dtype,
+                            static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int mlp_tp_swiglu_shard_fwd(const void* X, const void* Wgr, const void* Wur, const void* W2r,
+                            void* G, void* U, void* H, float* P, int64_t N, int64_t D, int64_t F,
+                            int32_t T, int32_t dtype, void* stream)
+{
+    if (int rc = check_swiglu_up(X, Wgr, Wur, G, U, H, N, D, F, T, dtype)) return rc;
+    if (int rc = check_down(H, W2r, P, N, D, F, T, dtype)) return rc;
+    {
+        const int64_t es = elem_size(dtype), Fs = F / T;
+        if (int rc = disjoint({{P, N * D * 4}}, {{X, N * D * es}, {Wgr, D * Fs * es},
+                                                  {Wur, D * Fs * es}, {G, N * Fs * es},
+                                                  {U, N * Fs * es}}))
+            return rc;
+        if (int rc = disjoint({{H, N * Fs * es}, {G, N * Fs * es}, {U, N * Fs * es}},
+                              {{W2r, Fs * D * es}}))
+            return rc;
+    }
+    if (N == 0) return MLP_TP_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    mlptp::launch_swiglu_up(X, Wgr, Wur, G, U, H, N, D, F / T, dtype, s);
+    if (int rc = launch_status()) return rc;
+    mlptp::launch_down_proj(H, W2r, P, N, D, F / T, dtype, s);
     return launch_status();
 }
 

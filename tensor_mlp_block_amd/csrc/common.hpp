@@ -41,6 +41,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 // Logistic function 1 / (1 + e^-x), stable at both ends (e^-x -> inf gives 0, -> 0 gives 1).
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// SiLU(z) = z * sigmoid(z), the gate nonlinearity of the gated MLP.
+__device__ __forceinline__ float silu_f(float z) { return z * sigmoidf_(z); }
+
 // GELU, tanh form: 0.5 z (1 + tanh(u)) with u = sqrt(2/pi) (z + 0.044715 z^3). Since
 // 0.5 (1 + tanh(u)) equals the logistic function at 2u, it is evaluated as z * sigmoid(2u),
 // which needs one exponential and saturates cleanly for large |z|.

@@ -55,14 +55,18 @@ inline void run_mfma(const void* A, const void* B, int64_t M, int64_t N, int64_t
                        static_cast<const uint16_t*>(B), M, N, K, lda, ldb, vecA, vecB, epi);
 }
 
+// N counts output columns; a dual epilogue takes two B operands (B2 non-null) whose tiles
+// share the workgroup's B region, so each tile covers BN / 2 output columns.
 template <class Cfg, bool A_KC, bool B_KC, class Epi>
 inline void run_dma(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int64_t lda,
-                    int64_t ldb, Epi epi, hipStream_t s)
+                    int64_t ldb, Epi epi, hipStream_t s, const void* B2 = nullptr)
 {
-    const int64_t tiles = ceil_div(M, Cfg::BM) * ceil_div(N, Cfg::BN);
+    constexpr int BNO = EpiIsDual<Epi>::value ? Cfg::BN / 2 : Cfg::BN;
+    const int64_t tiles = ceil_div(M, Cfg::BM) * ceil_div(N, BNO);
     hipLaunchKernelGGL((gemm_bf16_dma<Cfg, A_KC, B_KC, Epi>), dim3((uint32_t)tiles),
                        dim3(Cfg::NTHREADS), 0, s, static_cast<const uint16_t*>(A),
-                       static_cast<const uint16_t*>(B), M, N, K, lda, ldb, epi);
+                       static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2), M, N,
+                       K, lda, ldb, epi);
 }
 
 // Every bf16 product goes through here: the direct-to-LDS kernel when the shape allows it,

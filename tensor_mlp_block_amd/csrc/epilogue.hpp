@@ -119,9 +119,11 @@ __device__ __forceinline__ int valid4(int64_t row, int64_t col, int64_t M, int64
     return n < 4 ? (int)n : 4;
 }
 
-// Plain fp32 store: the row-parallel partial P^(r) (no b2 [Z 05]), weight gradients, dX^(r).
-struct EpiStoreF32 {
-    float* C;
+// Plain store as T: the row-parallel partial P^(r) in fp32 (no b2 [Z 05]), weight gradients,
+// dX^(r); in bf16, a staged gate pre-activation.
+template <class T>
+struct EpiStore {
+    T* C;
     int64_t ldc;
     int vec;
     using ColData = NoData;
@@ -142,6 +144,37 @@ struct EpiStoreF32 {
                                                int64_t N) const
     {
         apply(row, col, v, {}, {}, M, N);
+    }
+};
+using EpiStoreF32 = EpiStore<float>;
+
+// fp32 accumulation C += v: a down-projection adding its partial into one running buffer,
+// the sequential one-GPU form of the block-tail sum [Z 02]. Each element is read and written
+// by the same lane, so the update needs no atomics.
+struct EpiAccumF32 {
+    float* C;
+    int64_t ldc;
+    int vec;
+    using ColData = NoData;
+    using ElemData = Staged4<float>;
+    static constexpr bool kColData = false, kElemData = true;
+    __device__ __forceinline__ ColData col_load(int64_t, int64_t) const { return {}; }
+    __device__ __forceinline__ ElemData elem_load(int64_t row, int64_t col, int64_t M,
+                                                  int64_t N) const
+    {
+        const int n = valid4(row, col, M, N);
+        return n ? ElemData::load(C + row * ldc + col, n, vec) : ElemData::load(C, 0, false);
+    }
+    __device__ __forceinline__ void apply(int64_t row, int64_t col, f32x4 v, ColData, ElemData c,
+                                          int64_t M, int64_t N) const
+    {
+        const int n = valid4(row, col, M, N);
+        if (n) store4(C + row * ldc + col, c.get() + v, n, vec);
+    }
+    __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 v, int64_t M,
+                                               int64_t N) const
+    {
+        apply(row, col, v, {}, elem_load(row, col, M, N), M, N);
     }
 };
 
@@ -221,6 +254,72 @@ struct EpiActGrad {
                                                int64_t N) const
     {
         apply(row, col, v, {}, elem_load(row, col, M, N), M, N);
+    }
+};
+
+// Gated MLP [Z 08], fused form: the GEMM produced the gate g = X Wg^(r) and the up value
+// u = X Wu^(r) of the same four columns (the two projections are cut at the same columns);
+// H = SiLU(g) * u. G and U keep the pre-activations for the backward when non-null.
+template <class T>
+struct EpiSwiGLU {
+    T* H;  // [M, N]
+    T* G;  // [M, N] or nullptr
+    T* U;  // [M, N] or nullptr
+    int64_t ldc;
+    int vec;
+    static constexpr bool kDual = true;
+    using ColData = NoData;
+    static constexpr bool kColData = false;
+    __device__ __forceinline__ void apply_dual(int64_t row, int64_t col, f32x4 g, f32x4 u,
+                                               int64_t M, int64_t N) const
+    {
+        const int n = valid4(row, col, M, N);
+        if (!n) return;
+        if (G) store4(G + row * ldc + col, g, n, vec);
+        if (U) store4(U + row * ldc + col, u, n, vec);
+        f32x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = silu_f(g[e]) * u[e];
+        store4(H + row * ldc + col, h, n, vec);
+    }
+};
+
+// Gated MLP, second pass of the two-GEMM form: the GEMM produced u = X Wu^(r); the gate
+// values g were stored by the first pass in `gate` (which may be H itself: each element is
+// read before it is overwritten, by the same lane). H = SiLU(g) * u.
+template <class T>
+struct EpiGateMul {
+    const T* gate;  // [M, N]
+    T* U;           // [M, N] or nullptr
+    T* H;           // [M, N]
+    int64_t ldc;
+    int vec;
+    using ColData = NoData;
+    using ElemData = Staged4<T>;
+    static constexpr bool kColData = false, kElemData = true;
+    __device__ __forceinline__ ColData col_load(int64_t, int64_t) const { return {}; }
+    __device__ __forceinline__ ElemData elem_load(int64_t row, int64_t col, int64_t M,
+                                                  int64_t N) const
+    {
+        const int n = valid4(row, col, M, N);
+        return n ? ElemData::load(gate + row * ldc + col, n, vec) : ElemData::load(gate, 0, false);
+    }
+    __device__ __forceinline__ void apply(int64_t row, int64_t col, f32x4 u, ColData, ElemData g,
+                                          int64_t M, int64_t N) const
+    {
+        const int n = valid4(row, col, M, N);
+        if (!n) return;
+        if (U) store4(U + row * ldc + col, u, n, vec);
+        const f32x4 gv = g.get();
+        f32x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = silu_f(gv[e]) * u[e];
+        store4(H + row * ldc + col, h, n, vec);
+    }
+    __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 u, int64_t M,
+                                               int64_t N) const
+    {
+        apply(row, col, u, {}, elem_load(row, col, M, N), M, N);
     }
 };
 

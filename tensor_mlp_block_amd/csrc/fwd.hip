@@ -1,6 +1,8 @@
 // fwd.hip -- forward shard kernels: column-parallel up-projection with fused bias and
 // activation, and row-parallel down-projection to the fp32 partial.
 //
+// Also the gated (SwiGLU) up-projection and the accumulating form of the down-projection.
+//
 // Pages cited, as [tag section]:
 //   [Z] zwjcode.cn, "一层 MLP 太宽而放不下时怎样切？列并行、行并行与块尾归约"
 //   [J] jwzheng96.github.io, "张量并行 TP 与列并行 / 行并行的实现" (Megatron-LM tutorial ch. 7)
@@ -57,6 +59,61 @@ void launch_down_proj(const void* H, const void* W2r, float* P, int64_t N, int64
         run_bf16<true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
     else
         run_simt<true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
+}
+
+// P += H^(r) W2^(r): the shards of one GPU adding their partials into one running fp32 buffer
+// in turn, the sequential form of the block-tail sum [Z 02].
+void launch_down_proj_accumulate(const void* H, const void* W2r, float* P, int64_t N, int64_t D,
+                                 int64_t Fs, int dtype, hipStream_t s)
+{
+    EpiAccumF32 epi{P, D, (int)(D % 4 == 0)};
+    if (dtype == kBF16)
+        run_bf16<true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
+    else
+        run_simt<true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
+}
+
+// Gated up-projection [Z 08]: G = X Wg^(r), U = X Wu^(r) over the same columns,
+// H = SiLU(G) * U. GEMM view as the plain up-projection (A = X, B = the [D, Fs] weight).
+//   * bf16, shapes the direct-to-LDS kernel takes: one fused GEMM whose B tile holds 128
+//     columns of Wg^(r) and the same 128 columns of Wu^(r), so each X tile in LDS feeds both
+//     products and G, U never leave registers unless the caller keeps them.
+//   * otherwise two GEMMs: the gate goes to G (or, when the caller does not keep G, to H as a
+//     staging buffer), then the up GEMM's epilogue reads it back and writes H in place.
+template <class T>
+static void swiglu_up_typed(const void* X, const void* Wg, const void* Wu, void* G, void* U,
+                            void* H, int64_t N, int64_t D, int64_t Fs, hipStream_t s)
+{
+    const int vec = (Fs % 4 == 0);
+    T* h = static_cast<T*>(H);
+    T* g = static_cast<T*>(G);
+    T* u = static_cast<T*>(U);
+    if constexpr (sizeof(T) == 2) {
+        if (dma_eligible(true, false, N, Fs, D, D, Fs)) {
+            EpiSwiGLU<T> epi{h, g, u, Fs, vec};
+            run_dma<DmaTile256x256, true, false>(X, Wg, N, Fs, D, D, Fs, epi, s, Wu);
+            return;
+        }
+    }
+    T* gate = g ? g : h;
+    EpiStore<T> first{gate, Fs, vec};
+    EpiGateMul<T> second{gate, u, h, Fs, vec};
+    if constexpr (sizeof(T) == 2) {
+        run_bf16<true, false>(X, Wg, N, Fs, D, D, Fs, first, s);
+        run_bf16<true, false>(X, Wu, N, Fs, D, D, Fs, second, s);
+    } else {
+        run_simt<true, false>(X, Wg, N, Fs, D, D, Fs, first, s);
+        run_simt<true, false>(X, Wu, N, Fs, D, D, Fs, second, s);
+    }
+}
+
+void launch_swiglu_up(const void* X, const void* Wg, const void* Wu, void* G, void* U, void* H,
+                      int64_t N, int64_t D, int64_t Fs, int dtype, hipStream_t s)
+{
+    if (dtype == kBF16)
+        swiglu_up_typed<uint16_t>(X, Wg, Wu, G, U, H, N, D, Fs, s);
+    else
+        swiglu_up_typed<float>(X, Wg, Wu, G, U, H, N, D, Fs, s);
 }
 
 }  // namespace mlptp

@@ -138,11 +138,14 @@ __device__ __forceinline__ bf16x8 frag_mc(const MLPTP_LDS uint8_t* lds, int row0
 struct DmaCtx {
     const uint16_t* A;
     const uint16_t* B;
+    const uint16_t* B2;  // dual form only: the second B, loaded beside the first
     int64_t M, N, K, lda, ldb, m0, n0;
     int m_left, n_left, wave, lane;
 };
 
-template <class Cfg, bool A_KC, bool B_KC>
+// Loads of stage kt. In the dual form the B tile is two tiles of BN/2 columns, the same output
+// columns of B and of B2, side by side in LDS.
+template <class Cfg, bool A_KC, bool B_KC, bool DUAL>
 __device__ __forceinline__ void dma_issue(const DmaCtx& c, int64_t kt, MLPTP_LDS uint8_t* base)
 {
     const int64_t k0 = kt * Cfg::BK;
@@ -150,20 +153,29 @@ __device__ __forceinline__ void dma_issue(const DmaCtx& c, int64_t kt, MLPTP_LDS
     const uint16_t* a = A_KC ? c.A + c.m0 * c.lda + k0 : c.A + k0 * c.lda + c.m0;
     const uint16_t* b = B_KC ? c.B + c.n0 * c.ldb + k0 : c.B + k0 * c.ldb + c.n0;
     dma_tile<Cfg::BM, Cfg::NWAVES, A_KC>(a, c.lda, c.m_left, k_left, base, c.wave, c.lane);
-    dma_tile<Cfg::BN, Cfg::NWAVES, B_KC>(b, c.ldb, c.n_left, k_left, base + Cfg::A_BYTES, c.wave,
-                                         c.lane);
+    if constexpr (!DUAL) {
+        dma_tile<Cfg::BN, Cfg::NWAVES, B_KC>(b, c.ldb, c.n_left, k_left, base + Cfg::A_BYTES,
+                                             c.wave, c.lane);
+    } else {
+        constexpr int HB = Cfg::BN / 2;
+        const uint16_t* b2 = B_KC ? c.B2 + c.n0 * c.ldb + k0 : c.B2 + k0 * c.ldb + c.n0;
+        dma_tile<HB, Cfg::NWAVES, B_KC>(b, c.ldb, c.n_left, k_left, base + Cfg::A_BYTES, c.wave,
+                                        c.lane);
+        dma_tile<HB, Cfg::NWAVES, B_KC>(b2, c.ldb, c.n_left, k_left,
+                                        base + Cfg::A_BYTES + Cfg::B_BYTES / 2, c.wave, c.lane);
+    }
 }
 
 // One pipeline step: start the loads of stage `next_kt` (if >= 0) into `nxt`, then run the
 // MFMAs of the stage held in `cur`. `cur` and `nxt` are distinct stages; the __restrict__
 // qualifiers tell the compiler so, which lets it read `cur` while the loads into `nxt` are
 // still in flight instead of waiting for them first.
-template <class Cfg, bool A_KC, bool B_KC>
+template <class Cfg, bool A_KC, bool B_KC, bool DUAL>
 __device__ __attribute__((always_inline)) inline void dma_step(
     const DmaCtx& c, int64_t next_kt, const MLPTP_LDS uint8_t* __restrict__ cur,
     MLPTP_LDS uint8_t* __restrict__ nxt, f32x4 (&acc)[Cfg::FM][Cfg::FN], int wm, int wn)
 {
-    if (next_kt >= 0) dma_issue<Cfg, A_KC, B_KC>(c, next_kt, nxt);
+    if (next_kt >= 0) dma_issue<Cfg, A_KC, B_KC, DUAL>(c, next_kt, nxt);
     const MLPTP_LDS uint8_t* As = cur;
     const MLPTP_LDS uint8_t* Bs = cur + Cfg::A_BYTES;
 #pragma unroll
@@ -176,8 +188,18 @@ __device__ __attribute__((always_inline)) inline void dma_step(
         }
 #pragma unroll
         for (int j = 0; j < Cfg::FN; ++j) {
-            const int row = wn * Cfg::WTN + j * 16;
-            bfr[j] = B_KC ? frag_kc<Cfg::BN>(Bs, row, ks, c.lane) : frag_mc<Cfg::BN>(Bs, row, ks, c.lane);
+            if constexpr (!DUAL) {
+                const int row = wn * Cfg::WTN + j * 16;
+                bfr[j] = B_KC ? frag_kc<Cfg::BN>(Bs, row, ks, c.lane)
+                              : frag_mc<Cfg::BN>(Bs, row, ks, c.lane);
+            } else {
+                // Fragments 0 .. FN/2-1 from the first B tile, the rest from the second, at the
+                // same columns: acc[i][j] and acc[i][j + FN/2] hold the same outputs of B and B2.
+                constexpr int HB = Cfg::BN / 2, HF = Cfg::FN / 2;
+                const MLPTP_LDS uint8_t* Bh = Bs + (j / HF) * (Cfg::B_BYTES / 2);
+                const int row = wn * (Cfg::WTN / 2) + (j % HF) * 16;
+                bfr[j] = B_KC ? frag_kc<HB>(Bh, row, ks, c.lane) : frag_mc<HB>(Bh, row, ks, c.lane);
+            }
         }
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i)
@@ -187,11 +209,25 @@ __device__ __attribute__((always_inline)) inline void dma_step(
     }
 }
 
+// Whether an epilogue takes the dual form (two results per output element, from B and B2).
+template <class E, class = void>
+struct EpiIsDual : std::false_type {};
+template <class E>
+struct EpiIsDual<E, std::void_t<decltype(E::kDual)>> : std::bool_constant<E::kDual> {};
+
+// C[M, N] = A B, or in the dual form the pair (A B, A B2) handed to epi.apply_dual: one A tile
+// in LDS feeds both products, as the gated MLP's gate and up projections need [Z 08].
 template <class Cfg, bool A_KC, bool B_KC, class Epi>
 __global__ __launch_bounds__(Cfg::NTHREADS, 1) void gemm_bf16_dma(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int64_t M, int64_t N,
-    int64_t K, int64_t lda, int64_t ldb, Epi epi)
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+    const uint16_t* __restrict__ B2, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+    Epi epi)
 {
+    constexpr bool DUAL = EpiIsDual<Epi>::value;
+    constexpr int BNO = DUAL ? Cfg::BN / 2 : Cfg::BN;    // output columns per tile
+    constexpr int WTNO = DUAL ? Cfg::WTN / 2 : Cfg::WTN;  // output columns per wave
+    static_assert(!DUAL || (Cfg::FN % 2 == 0 && (Cfg::BN / 2) % 128 == 0),
+                  "dual tiles are two halves of 128k columns");
     __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * Cfg::STAGE_BYTES];
     // C-style cast: generic -> LDS address space (smem_raw is an LDS variable).
     MLPTP_LDS uint8_t* smem = (MLPTP_LDS uint8_t*)(smem_raw);
@@ -200,12 +236,12 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void gemm_bf16_dma(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave % Cfg::WAVES_M, wn = wave / Cfg::WAVES_M;
 
-    const int64_t tiles_m = ceil_div(M, Cfg::BM), tiles_n = ceil_div(N, Cfg::BN);
+    const int64_t tiles_m = ceil_div(M, Cfg::BM), tiles_n = ceil_div(N, BNO);
     int64_t tm, tn;
     tile_coords<Cfg::GROUP_M>(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const int64_t m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+    const int64_t m0 = tm * Cfg::BM, n0 = tn * BNO;
     const int m_left = (int)((M - m0) < Cfg::BM ? (M - m0) : Cfg::BM);
-    const int n_left = (int)((N - n0) < Cfg::BN ? (N - n0) : Cfg::BN);
+    const int n_left = (int)((N - n0) < BNO ? (N - n0) : BNO);
 
     f32x4 acc[Cfg::FM][Cfg::FN];
 #pragma unroll
@@ -217,23 +253,23 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void gemm_bf16_dma(
     // under the MFMAs instead of stalling the epilogue between stores.
     const int frow = lane & 15, fchunk = lane >> 4;
     typename Epi::ColData cdat[Cfg::FN];
-    if constexpr (Epi::kColData) {
+    if constexpr (!DUAL && Epi::kColData) {
 #pragma unroll
         for (int j = 0; j < Cfg::FN; ++j)
             cdat[j] = epi.col_load(n0 + wn * Cfg::WTN + j * 16 + 4 * fchunk, N);
     }
 
     const int64_t nk = ceil_div(K, Cfg::BK);
-    const DmaCtx ctx{A, B, M, N, K, lda, ldb, m0, n0, m_left, n_left, wave, lane};
+    const DmaCtx ctx{A, B, B2, M, N, K, lda, ldb, m0, n0, m_left, n_left, wave, lane};
 
-    dma_issue<Cfg, A_KC, B_KC>(ctx, 0, smem);
+    dma_issue<Cfg, A_KC, B_KC, DUAL>(ctx, 0, smem);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
     for (int64_t kt = 0; kt < nk; ++kt) {
         MLPTP_LDS uint8_t* cur = smem + (kt & 1) * Cfg::STAGE_BYTES;
         MLPTP_LDS uint8_t* nxt = smem + ((kt + 1) & 1) * Cfg::STAGE_BYTES;
-        dma_step<Cfg, A_KC, B_KC>(ctx, kt + 1 < nk ? kt + 1 : -1, cur, nxt, acc, wm, wn);
+        dma_step<Cfg, A_KC, B_KC, DUAL>(ctx, kt + 1 < nk ? kt + 1 : -1, cur, nxt, acc, wm, wn);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the next stage
         __syncthreads();
     }
@@ -241,13 +277,21 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void gemm_bf16_dma(
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
         const int64_t row = m0 + wm * Cfg::WTM + i * 16 + frow;
+        if constexpr (DUAL) {
 #pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) {
-            const int64_t col = n0 + wn * Cfg::WTN + j * 16 + 4 * fchunk;
-            if constexpr (Epi::kColData)
-                epi.apply(row, col, acc[i][j], cdat[j], {}, M, N);
-            else
-                epi(row, col, acc[i][j], M, N);
+            for (int j = 0; j < Cfg::FN / 2; ++j) {
+                const int64_t col = n0 + wn * WTNO + j * 16 + 4 * fchunk;
+                epi.apply_dual(row, col, acc[i][j], acc[i][j + Cfg::FN / 2], M, N);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j) {
+                const int64_t col = n0 + wn * Cfg::WTN + j * 16 + 4 * fchunk;
+                if constexpr (Epi::kColData)
+                    epi.apply(row, col, acc[i][j], cdat[j], {}, M, N);
+                else
+                    epi(row, col, acc[i][j], M, N);
+            }
         }
     }
 }

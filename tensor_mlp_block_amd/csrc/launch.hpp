@@ -21,6 +21,15 @@ void launch_up_proj(const void* X, const void* W1r, const void* b1r, void* Z, vo
 void launch_down_proj(const void* H, const void* W2r, float* P, int64_t N, int64_t D, int64_t Fs,
                       int dtype, hipStream_t s);
 
+// P += H W2r (fp32 accumulation into an existing partial).
+void launch_down_proj_accumulate(const void* H, const void* W2r, float* P, int64_t N, int64_t D,
+                                 int64_t Fs, int dtype, hipStream_t s);
+
+// Gated up-projection: G = X Wg, U = X Wu (same columns), H = SiLU(G) * U. X [N, D], Wg/Wu
+// [D, Fs], G/U (nullable)/H [N, Fs].
+void launch_swiglu_up(const void* X, const void* Wg, const void* Wu, void* G, void* U, void* H,
+                      int64_t N, int64_t D, int64_t Fs, int dtype, hipStream_t s);
+
 // dZ = (dY W2r^T) * phi'(Z). dY [N, D], W2r [Fs, D], Z/dZ [N, Fs].
 void launch_bwd_dz(const void* dY, const void* W2r, const void* Z, void* dZ, int64_t N, int64_t D,
                    int64_t Fs, int dtype, int act, hipStream_t s);

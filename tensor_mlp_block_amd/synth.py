@@ -13,6 +13,8 @@ block is drawn from its own ``torch.Generator('cpu')`` seeded with a splitmix64 
   is bit-identical to the same slice of the full weight, and computing it does not require
   drawing the other shards ("slice one fixed full weight", not a seed per rank: zwjcode.cn,
   "一层 MLP 太宽而放不下时怎样切？列并行、行并行与块尾归约", section 09);
+* Wg [D, F] and Wu [D, F] (the gated form's gate and up weights): as W1, blocks of ``BLOCK``
+  columns, each under its own tag;
 * W2 [F, D]: blocks of ``BLOCK`` rows (the row shard is a slice of the full weight);
 * b2 [D]: a single block.
 
@@ -31,7 +33,7 @@ from .workloads import Workload
 
 BLOCK = 128
 
-TAG_X, TAG_W1, TAG_B1, TAG_W2, TAG_B2, TAG_DY = 1, 2, 3, 4, 5, 6
+TAG_X, TAG_W1, TAG_B1, TAG_W2, TAG_B2, TAG_DY, TAG_WG, TAG_WU = 1, 2, 3, 4, 5, 6, 7, 8
 
 _MASK64 = (1 << 64) - 1
 
@@ -116,6 +118,16 @@ def gen_X(w: Workload) -> torch.Tensor:
 def gen_W1(w: Workload, c0: int = 0, c1: int | None = None) -> torch.Tensor:
     c1 = w.F if c1 is None else c1
     return _finish(blocked_slice(w.seed, TAG_W1, (w.D, w.F), 1, c0, c1, w.dist, w.w_std), w)
+
+
+def gen_Wg(w: Workload, c0: int = 0, c1: int | None = None) -> torch.Tensor:
+    c1 = w.F if c1 is None else c1
+    return _finish(blocked_slice(w.seed, TAG_WG, (w.D, w.F), 1, c0, c1, w.dist, w.w_std), w)
+
+
+def gen_Wu(w: Workload, c0: int = 0, c1: int | None = None) -> torch.Tensor:
+    c1 = w.F if c1 is None else c1
+    return _finish(blocked_slice(w.seed, TAG_WU, (w.D, w.F), 1, c0, c1, w.dist, w.w_std), w)
 
 
 def gen_b1(w: Workload, c0: int = 0, c1: int | None = None) -> torch.Tensor:

@@ -18,7 +18,7 @@ class Workload:
     D: int
     F: int
     T: int
-    act: str                    # "relu" | "gelu_tanh" | "gelu_erf" | "identity"
+    act: str                    # "relu" | "gelu_tanh" | "gelu_erf" | "identity" | "swiglu"
     dtype: str                  # "f32" (exact integer data) | "bf16"
     seed: int
     dist: str                   # "int": uniform integers in [-2, 2]; "normal": N(0, std^2)
@@ -61,6 +61,18 @@ GPT3_175B_T8 = Workload("gpt3_175b_mlp_n2048_d12288_f49152_t8", N=2048, D=12288,
 LLAMA70B_SHARD_T8_BWD = LLAMA70B_SHARD_T8.with_(
     name="llama3_70b_ffn_shard_bwd_n4096_d8192_f28672_t8", dy_seed=505)
 
-ALL = (INT_EXACT, GPT2_MEDIUM_T2, LLAMA70B_SHARD_T8, GPT3_175B_T8, LLAMA70B_SHARD_T8_BWD)
+# The gated (SwiGLU) form of the same Llama-3-70B FFN shard: gate and up weights [8192, 28672]
+# cut 8 ways at the same columns, no biases.
+LLAMA70B_SWIGLU_SHARD_T8 = Workload("llama3_70b_swiglu_shard_n4096_d8192_f28672_t8", N=4096,
+                                    D=8192, F=28672, T=8, act="swiglu", dtype="bf16",
+                                    seed=606, dist="normal", bias=False)
+
+# The MLP shape of the pages' PyTorch example (d_model = 4096, d_ff = 11008, x [2, 128, 4096]),
+# for the shard-count sweep: T = 1, 2, 4, 8 all divide 11008.
+PAGE_EXAMPLE_MLP = Workload("page_example_mlp_n256_d4096_f11008", N=256, D=4096, F=11008, T=1,
+                            act="gelu_tanh", dtype="bf16", seed=707, dist="normal")
+
+ALL = (INT_EXACT, GPT2_MEDIUM_T2, LLAMA70B_SHARD_T8, GPT3_175B_T8, LLAMA70B_SHARD_T8_BWD,
+       LLAMA70B_SWIGLU_SHARD_T8, PAGE_EXAMPLE_MLP)
 
 BY_NAME = {w.name: w for w in ALL}

@@ -121,6 +121,59 @@ def test_partial_reduce_checks(lib):
     assert _reduce(lib, [A, B], Y=A, N=0) == mt.OK                 # exact in-place is allowed
 
 
+def _scatter(lib, ptrs, r, T=None, b2=None, b2_dtype=mt.F32, Y=G, N=10, D=8):
+    import ctypes
+    T = len(ptrs) if T is None else T
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    return lib.mlp_tp_partial_reduce_scatter(ctypes.cast(arr, ctypes.c_void_p), T, r, b2,
+                                             b2_dtype, Y, N, D, S)
+
+
+def test_token_slices_match_the_oracle():
+    # [Z 04] reduce-scatter layout: the library's slice bounds are the oracle's.
+    import oracle
+    for N, T in [(10, 4), (4096, 8), (3, 8), (0, 2), (7, 1)]:
+        for r in range(T):
+            assert mt.mlp_tp_token_slice(N, T, r) == oracle.token_slice(N, T, r)
+    with pytest.raises(mt.MlpTpError):
+        mt.mlp_tp_token_slice(4, 2, 2)
+    assert mt.load().mlp_tp_token_slice(4, 2, 0, None, None) == mt.E_NULL
+
+
+def test_partial_reduce_scatter_checks(lib):
+    assert _scatter(lib, [A, B], r=2) == mt.E_SHAPE                  # r outside [0, T)
+    assert _scatter(lib, [A, B], r=-1) == mt.E_SHAPE
+    assert _scatter(lib, [A, None], r=0) == mt.E_NULL
+    assert _scatter(lib, [A, B + 4], r=0) == mt.E_ALIGN
+    assert _scatter(lib, [A, B], r=0, Y=A + 16) == mt.E_ALIAS        # not the slice's own rows
+    assert _scatter(lib, [A, B], r=1, Y=A) == mt.E_ALIAS             # P[0] rows 0.., slice 1 at row 5
+    assert _scatter(lib, [A, B], r=0, b2=G) == mt.E_ALIAS            # Yr over b2
+    assert _scatter(lib, [A, B], r=1, N=1) == mt.OK                  # empty slice: no-op
+    assert _scatter(lib, [A, B], r=0, N=0) == mt.OK
+
+
+def test_accumulate_and_gated_checks(lib):
+    acc = lib.mlp_tp_down_proj_accumulate
+    assert acc(A, B, None, 4, 8, 16, 2, mt.BF16, S) == mt.E_NULL
+    assert acc(A, B, A, 4, 8, 16, 2, mt.BF16, S) == mt.E_ALIAS
+    assert acc(A, B, E, 4, 8, 16, 3, mt.BF16, S) == mt.E_INDIVISIBLE
+    assert acc(A, B, E, 0, 8, 16, 2, mt.BF16, S) == mt.OK
+    up = lib.mlp_tp_swiglu_up_proj
+    assert up(A, B, None, None, None, Dp, 4, 8, 16, 2, mt.BF16, S) == mt.E_NULL   # Wur
+    assert up(A, B, C, None, None, None, 4, 8, 16, 2, mt.BF16, S) == mt.E_NULL    # H
+    assert up(A, B, C, Dp, None, Dp, 4, 8, 16, 2, mt.BF16, S) == mt.E_ALIAS       # G over H
+    assert up(A, B, C, None, B, Dp, 4, 8, 16, 2, mt.BF16, S) == mt.E_ALIAS        # U over Wgr
+    assert up(A, B, C, None, None, Dp, 4, 8, 18, 4, mt.BF16, S) == mt.E_INDIVISIBLE
+    assert up(A, B, C, None, None, Dp + 2, 4, 8, 16, 2, mt.BF16, S) == mt.E_ALIGN
+    assert up(A, B, C, None, None, Dp, 4, 8, 16, 2, 7, S) == mt.E_DTYPE
+    assert up(A, B, C, None, None, Dp, 0, 8, 16, 2, mt.BF16, S) == mt.OK
+    fwd = lib.mlp_tp_swiglu_shard_fwd
+    assert fwd(A, B, C, None, None, None, Dp, E, 4, 8, 16, 2, mt.BF16, S) == mt.E_NULL  # W2r
+    assert fwd(A, B, C, G, None, None, Dp, C, 4, 8, 16, 2, mt.BF16, S) == mt.E_ALIAS   # P over Wur
+    assert fwd(A, B, C, G, None, None, G, E, 4, 8, 16, 2, mt.BF16, S) == mt.E_ALIAS    # H over W2r
+    assert fwd(A, B, C, G, None, None, Dp, E, 0, 8, 16, 2, mt.BF16, S) == mt.OK
+
+
 def test_workspace_query_uses_global_sizes(lib):
     """[C 先弄清楚]: a [8192, 32768] weight split 8 ways gives [8192, 4096] per card; the
     library derives Fs = F / T from the global F itself. The db1 workspace holds one fp32 row
