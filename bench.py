@@ -9,7 +9,11 @@ forward shard through the C ABI: the column-parallel up-projection with fused bi
 
 Also measured in the same run, each over its own timed loop (reported under "rows"): the
 block-tail reduction of 8 fp32 partials [2048, 12288] with b2 (the GPT-3-175B layer's tail),
-the shard backward at the Llama shape, and the sum of 8 dX partials [4096, 8192].
+the shard backward at the Llama shape, the sum of 8 dX partials [4096, 8192], the gated
+(SwiGLU) shard forward, the whole GPT-3-175B layer on one GPU with its tail as separate
+partials + reduce, as an accumulating down-projection, and overlapped with the last shard's
+down-projection, one token slice of that tail (reduce-scatter layout), and the shard forward
+at the Llama shape for T = 1, 2, 4, 8.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -267,7 +271,119 @@ def measure_rows(torch, mt, synth, workloads, dev, X, W1, b1, W2, H, w):
                      "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes": nbytes}
     log(f"[bench] sum dX T=8 [4096,8192]: {ms:.4f} ms, {res['sum_dx']['GB/s']} GB/s")
-    del parts
+    del parts, dX, dY, ws
+
+    res.update(measure_next_rows(torch, mt, synth, workloads, dev, g))
+    return res
+
+
+def _randn_bf16(torch, shape, std, g, dev):
+    return (torch.randn(shape, generator=g, device=dev) * std).to(torch.bfloat16)
+
+
+def measure_next_rows(torch, mt, synth, workloads, dev, g):
+    """The gated shard, the three forms of the GPT-3-175B layer's block tail, one token slice of
+    that tail, and the shard-count sweep at the Llama shape. Weights for these timing rows are
+    drawn on the GPU (torch.randn, the workloads' distributions); parity is the tests' job."""
+    res = {}
+
+    # Gated (SwiGLU) shard of the Llama-3-70B FFN: gate and up in one dual GEMM, then down.
+    w = workloads.LLAMA70B_SWIGLU_SHARD_T8
+    N, D, F, T, Fs = w.N, w.D, w.F, w.T, w.Fs
+    X = _randn_bf16(torch, (N, D), 1.0, g, dev)
+    Wg, Wu = _randn_bf16(torch, (D, Fs), 0.02, g, dev), _randn_bf16(torch, (D, Fs), 0.02, g, dev)
+    W2 = _randn_bf16(torch, (Fs, D), 0.02, g, dev)
+    H = torch.empty((N, Fs), dtype=torch.bfloat16, device=dev)
+    P = torch.empty((N, D), device=dev)
+    ms = _time_loop(torch, lambda: mt.mlp_tp_swiglu_shard_fwd(X, Wg, Wu, W2, None, None, H, P, N,
+                                                              D, F, T, mt.BF16), 20)
+    flop = 6.0 * N * D * Fs
+    res["gated_shard_fwd"] = {"workload": w.name, "ms": round(ms, 5),
+                              "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1),
+                              "frac_mfma": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    log(f"[bench] gated shard fwd: {ms:.4f} ms, {res['gated_shard_fwd']['TFLOP/s']} TFLOP/s")
+    del X, Wg, Wu, W2, H, P
+
+    # The GPT-3-175B MLP layer on one GPU: 8 shards of F/T = 6144 in sequence and the tail,
+    #   separate: 8 fp32 partials, then the T-way reduce with b2;
+    #   accumulate: each down-projection adds into one buffer seeded with b2;
+    #   overlapped: shards 0-6 as in `separate`, shard 7's down-projection in token chunks with
+    #   each finished chunk's tail on a second stream.
+    w = workloads.GPT3_175B_T8
+    N, D, F, T, Fs = w.N, w.D, w.F, w.T, w.Fs
+    X = _randn_bf16(torch, (N, D), 1.0, g, dev)
+    W1s = [_randn_bf16(torch, (D, Fs), 0.02, g, dev) for _ in range(T)]
+    b1s = [_randn_bf16(torch, (Fs,), 0.02, g, dev) for _ in range(T)]
+    W2s = [_randn_bf16(torch, (Fs, D), 0.02, g, dev) for _ in range(T)]
+    b2 = _randn_bf16(torch, (D,), 0.02, g, dev)
+    b2f = b2.float()
+    H = torch.empty((N, Fs), dtype=torch.bfloat16, device=dev)
+    parts = [torch.empty((N, D), device=dev) for _ in range(T)]
+    Y = torch.empty((N, D), device=dev)
+    side = torch.cuda.Stream(device=dev)
+    chunk = 1024  # two chunks: each chunk's GEMM still fills most of the CUs
+
+    def separate():
+        for r in range(T):
+            mt.mlp_tp_shard_fwd(X, W1s[r], b1s[r], W2s[r], H, None, parts[r], N, D, F, T, mt.BF16,
+                                w.act)
+        mt.mlp_tp_partial_reduce(parts, T, b2, mt.BF16, Y, N, D)
+
+    def accumulate():
+        Y.copy_(b2f.expand(N, D))
+        for r in range(T):
+            mt.mlp_tp_up_proj(X, W1s[r], b1s[r], None, H, N, D, F, T, mt.BF16, w.act)
+            mt.mlp_tp_down_proj_accumulate(H, W2s[r], Y, N, D, F, T, mt.BF16)
+
+    def overlapped():
+        for r in range(T - 1):
+            mt.mlp_tp_shard_fwd(X, W1s[r], b1s[r], W2s[r], H, None, parts[r], N, D, F, T, mt.BF16,
+                                w.act)
+        mt.mlp_tp_up_proj(X, W1s[T - 1], b1s[T - 1], None, H, N, D, F, T, mt.BF16, w.act)
+        mt.mlp_tp_down_proj_overlap_tail(H, W2s[T - 1], parts, T, T - 1, b2, mt.BF16, Y, N, D, F,
+                                         mt.BF16, chunk, tail_stream=side)
+
+    flop = 4.0 * N * D * F  # all 8 shards' GEMMs
+    layer = {"workload": w.name, "flop": flop, "tail_chunk_rows": chunk}
+    for name, fn in (("separate", separate), ("accumulate", accumulate),
+                     ("overlapped", overlapped)):
+        ms = _time_loop(torch, fn, 10)
+        layer[name] = {"ms": round(ms, 4), "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1)}
+        log(f"[bench] gpt3 layer ({name}): {ms:.4f} ms")
+    res["gpt3_layer"] = layer
+
+    # One token slice of that tail (reduce-scatter layout): rank 0's N / T rows.
+    row0, rows = mt.mlp_tp_token_slice(N, T, 0)
+    Yr = torch.empty((rows, D), device=dev)
+    ms = _time_loop(torch, lambda: mt.mlp_tp_partial_reduce_scatter(parts, T, 0, b2, mt.BF16, Yr,
+                                                                    N, D), 20)
+    nbytes = (T + 1) * 4.0 * rows * D + 2.0 * D
+    res["reduce_scatter_slice"] = {"workload": w.name, "T": T, "rows": rows, "ms": round(ms, 5),
+                                   "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                   "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                   "algorithmic_bytes": nbytes}
+    log(f"[bench] reduce-scatter slice: {ms:.4f} ms, {res['reduce_scatter_slice']['GB/s']} GB/s")
+    del X, W1s, b1s, W2s, H, parts, Y, Yr
+
+    # Shard count sweep at the Llama shape: one rank's forward for T = 1, 2, 4, 8.
+    w = workloads.LLAMA70B_SHARD_T8
+    N, D, F = w.N, w.D, w.F
+    X = _randn_bf16(torch, (N, D), 1.0, g, dev)
+    sweep = {}
+    for T in (1, 2, 4, 8):
+        Fs = F // T
+        W1 = _randn_bf16(torch, (D, Fs), 0.02, g, dev)
+        b1 = _randn_bf16(torch, (Fs,), 0.02, g, dev)
+        W2 = _randn_bf16(torch, (Fs, D), 0.02, g, dev)
+        H = torch.empty((N, Fs), dtype=torch.bfloat16, device=dev)
+        P = torch.empty((N, D), device=dev)
+        ms = _time_loop(torch, lambda: mt.mlp_tp_shard_fwd(X, W1, b1, W2, H, None, P, N, D, F, T,
+                                                           mt.BF16, w.act), 10)
+        tf = 4.0 * N * D * Fs / (ms * 1e-3) / 1e12
+        sweep[str(T)] = {"Fs": Fs, "ms": round(ms, 4), "TFLOP/s": round(tf, 1)}
+        log(f"[bench] T={T} shard fwd: {ms:.4f} ms, {tf:.1f} TFLOP/s")
+        del W1, b1, W2, H, P
+    res["shard_count_sweep"] = {"workload": w.name, "by_T": sweep}
     return res
 
 

@@ -72,6 +72,9 @@ extern "C" {
 /* Largest shard count mlp_tp_partial_reduce accepts in one call. */
 #define MLP_TP_MAX_REDUCE_T 64
 
+/* Most token chunks one overlapped block-tail call splits its rows into. */
+#define MLP_TP_MAX_TAIL_CHUNKS 256
+
 /*
  * Column-parallel up-projection with fused bias and activation [Z 02], [Z 05], [U 3.8]:
  *     Z = X . W1r + b1r   (fp32 accumulate),   H = phi(Z).
@@ -164,6 +167,34 @@ int mlp_tp_partial_reduce_scatter(const float* const* P, int32_t T, int32_t r, c
  */
 int mlp_tp_down_proj_accumulate(const void* H, const void* W2r, float* P, int64_t N, int64_t D,
                                 int64_t F, int32_t T, int32_t dtype, void* stream);
+
+/*
+ * Row-parallel down-projection of rank r overlapped with the block tail [U 3.8]: on one GPU,
+ * the last shard's GEMM and the reduction of the finished token rows run at the same time,
+ * the local form of overlapping the tail's all-reduce with the rest of the layer. The token
+ * rows are cut into chunks of chunk_rows:
+ *     P[r][chunk]  = H[chunk] . W2r                                   on `stream`;
+ *     Y[chunk]     = (((P[0] + P[1]) + ...) + P[T-1])[chunk] + b2      on `tail_stream`,
+ * the reduction of chunk c waiting only for the GEMM of chunk c.
+ *   H [N, Fs], W2r [Fs, D]: dtype; Fs = F / T as for mlp_tp_down_proj.
+ *   P   HOST array of T device pointers to float [N, D] partials. P[r] is written here; every
+ *       other partial must be complete before work queued after this call on either stream
+ *       could read it (e.g. computed earlier on `stream`).
+ *   b2  [D] of b2_dtype or NULL; Y [N, D] float, may be exactly equal to any P[s].
+ *   chunk_rows > 0, at most MLP_TP_MAX_TAIL_CHUNKS chunks.
+ *   stream, tail_stream  HIP streams (may be the same; then nothing overlaps). On return, work
+ *       queued on `stream` after this call sees Y complete.
+ * The library keeps a small pool of HIP events per device for the cross-stream waits
+ * (created on first use, never device memory); calls from several host threads are
+ * serialised while they enqueue.
+ * Errors: those of mlp_tp_down_proj and mlp_tp_partial_reduce, E_SHAPE (r outside [0, T),
+ * chunk_rows <= 0, too many chunks), E_ALIAS (partials overlapping each other, Y overlapping
+ * H, W2r, b2 or a partial other than exactly), E_HIP.
+ */
+int mlp_tp_down_proj_overlap_tail(const void* H, const void* W2r, const float* const* P,
+                                  int32_t T, int32_t r, const void* b2, int32_t b2_dtype, float* Y,
+                                  int64_t N, int64_t D, int64_t F, int32_t dtype,
+                                  int64_t chunk_rows, void* stream, void* tail_stream);
 
 /*
  * Gated (SwiGLU) up-projection [Z 08]: the gate and up projections are cut at the SAME columns,

@@ -57,6 +57,8 @@ def load() -> ctypes.CDLL:
         "mlp_tp_partial_reduce_scatter": ([vp, i32, i32, vp, i32, vp, i64, i64, vp],
                                           ctypes.c_int),
         "mlp_tp_down_proj_accumulate": ([vp, vp, vp, i64, i64, i64, i32, i32, vp], ctypes.c_int),
+        "mlp_tp_down_proj_overlap_tail": ([vp, vp, vp, i32, i32, vp, i32, vp, i64, i64, i64, i32,
+                                           i64, vp, vp], ctypes.c_int),
         "mlp_tp_swiglu_up_proj": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp],
                                   ctypes.c_int),
         "mlp_tp_swiglu_shard_fwd": ([vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
@@ -157,6 +159,19 @@ def mlp_tp_down_proj_accumulate(H, W2r, P, N, D, F, T, dtype, stream=None):
     rc = load().mlp_tp_down_proj_accumulate(_ptr(H), _ptr(W2r), _ptr(P), N, D, F, T, dtype,
                                             _stream(stream))
     return _check(rc, "mlp_tp_down_proj_accumulate")
+
+
+def mlp_tp_down_proj_overlap_tail(H, W2r, P, T, r, b2, b2_dtype, Y, N, D, F, dtype, chunk_rows,
+                                  stream=None, tail_stream=None):
+    """P[r] = H W2r in token chunks on `stream`, the block tail of each finished chunk on
+    `tail_stream` (default: the same stream)."""
+    ptrs = (ctypes.c_void_p * max(1, len(P)))(*[_ptr(p) for p in P])
+    s0 = _stream(stream)
+    s1 = _stream(tail_stream) if tail_stream is not None else s0
+    rc = load().mlp_tp_down_proj_overlap_tail(_ptr(H), _ptr(W2r), ctypes.cast(ptrs, ctypes.c_void_p),
+                                              T, r, _ptr(b2), b2_dtype, _ptr(Y), N, D, F, dtype,
+                                              chunk_rows, s0, s1)
+    return _check(rc, "mlp_tp_down_proj_overlap_tail")
 
 
 def mlp_tp_swiglu_up_proj(X, Wgr, Wur, G, U, H, N, D, F, T, dtype, stream=None):

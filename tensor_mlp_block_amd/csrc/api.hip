@@ -12,6 +12,10 @@
 
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <vector>
+
 namespace {
 
 using mlptp::kBF16;
@@ -77,6 +81,28 @@ int disjoint(std::initializer_list<Span> outs, std::initializer_list<Span> ins)
 int launch_status()
 {
     return hipGetLastError() == hipSuccess ? MLP_TP_OK : MLP_TP_E_HIP;
+}
+
+// Cross-stream ordering of the overlapped block tail needs HIP events. They are synchronisation
+// objects, not device memory: a pool per device, created on first use (timing disabled) and
+// kept until the process ends. Calls hold the mutex while they enqueue, so calls from several
+// host threads never share an event between a record and its wait.
+std::mutex g_event_mu;
+std::map<int, std::vector<hipEvent_t>> g_events;
+
+// n events of the current device in *out; MLP_TP_E_HIP if HIP cannot create them.
+int pooled_events(int n, hipEvent_t** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MLP_TP_E_HIP;
+    std::vector<hipEvent_t>& pool = g_events[dev];
+    while ((int)pool.size() < n) {
+        hipEvent_t e;
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return MLP_TP_E_HIP;
+        pool.push_back(e);
+    }
+    *out = pool.data();
+    return MLP_TP_OK;
 }
 
 int check_up(const void* X, const void* W1r, const void* b1r, void* Z, void* H, int64_t N,
@@ -239,6 +265,52 @@ int mlp_tp_down_proj_accumulate(const void* H, const void* W2r, float* P, int64_
     if (N == 0) return MLP_TP_OK;
     mlptp::launch_down_proj_accumulate(H, W2r, P, N, D, F / T, dtype,
                                        static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int mlp_tp_down_proj_overlap_tail(const void* H, const void* W2r, const float* const* P,
+                                  int32_t T, int32_t r, const void* b2, int32_t b2_dtype, float* Y,
+                                  int64_t N, int64_t D, int64_t F, int32_t dtype,
+                                  int64_t chunk_rows, void* stream, void* tail_stream)
+{
+    if (!P) return MLP_TP_E_NULL;
+    if (T < 1 || T > MLP_TP_MAX_REDUCE_T || r < 0 || r >= T) return MLP_TP_E_SHAPE;
+    if (int rc = check_down(H, W2r, P[r], N, D, F, T, dtype)) return rc;
+    if (int rc = check_reduce(P, T, b2, b2_dtype, Y, N, D)) return rc;
+    if (chunk_rows <= 0) return MLP_TP_E_SHAPE;
+    const int64_t chunks = (N + chunk_rows - 1) / chunk_rows;
+    if (chunks > MLP_TP_MAX_TAIL_CHUNKS) return MLP_TP_E_SHAPE;
+    const int64_t es = elem_size(dtype), Fs = F / T, bytes = N * D * 4;
+    for (int32_t s = 0; s < T; ++s) {
+        if (P[s] != Y && overlap({Y, bytes}, {P[s], bytes})) return MLP_TP_E_ALIAS;
+        if (s != r && overlap({P[r], bytes}, {P[s], bytes})) return MLP_TP_E_ALIAS;
+    }
+    if (int rc = disjoint({{Y, bytes}}, {{H, N * Fs * es}, {W2r, Fs * D * es}})) return rc;
+    if (b2 && overlap({Y, bytes}, {b2, D * elem_size(b2_dtype)})) return MLP_TP_E_ALIAS;
+    if (N == 0) return MLP_TP_OK;
+
+    const hipStream_t s0 = static_cast<hipStream_t>(stream);
+    const hipStream_t s1 = static_cast<hipStream_t>(tail_stream);
+    std::lock_guard<std::mutex> lock(g_event_mu);
+    hipEvent_t* ev = nullptr;
+    if (int rc = pooled_events((int)chunks + 1, &ev)) return rc;
+    float* Pr = const_cast<float*>(P[r]);
+    const char* Hb = static_cast<const char*>(H);
+    const float* Ps[MLP_TP_MAX_REDUCE_T];
+    for (int64_t c = 0; c < chunks; ++c) {
+        const int64_t row0 = c * chunk_rows;
+        const int64_t rows = (N - row0) < chunk_rows ? (N - row0) : chunk_rows;
+        // P[r] rows [row0, row0 + rows) on the compute stream ...
+        mlptp::launch_down_proj(Hb + row0 * Fs * es, W2r, Pr + row0 * D, rows, D, Fs, dtype, s0);
+        if (hipEventRecord(ev[c], s0) != hipSuccess) return MLP_TP_E_HIP;
+        // ... then the block tail of those rows on the tail stream once they are written.
+        if (hipStreamWaitEvent(s1, ev[c], 0) != hipSuccess) return MLP_TP_E_HIP;
+        for (int32_t s = 0; s < T; ++s) Ps[s] = P[s] + row0 * D;
+        mlptp::launch_partial_reduce(Ps, T, b2, b2_dtype, Y + row0 * D, rows, D, s1);
+    }
+    // Join: work queued on the compute stream after this call sees Y complete.
+    if (hipEventRecord(ev[chunks], s1) != hipSuccess) return MLP_TP_E_HIP;
+    if (hipStreamWaitEvent(s0, ev[chunks], 0) != hipSuccess) return MLP_TP_E_HIP;
     return launch_status();
 }
 

@@ -8,9 +8,9 @@
 // row-parallel outputs performs [Z 02], [Z 04], with b2 added exactly once after the sum
 // [Z 05], [U 3.8]. The work is pure streaming: T fp32 reads and one fp32 write per element,
 // so it is bound by HBM bandwidth. Each thread handles 16-byte vectors; the T loads of one
-// vector are issued back to back so T independent 16-byte requests are in flight per
-// thread, and the streaming loads/stores are marked non-temporal so they do not evict
-// anything useful from the caches.
+// vector are issued back to back, for several vectors per thread, so many independent 16-byte
+// requests are in flight per thread, and the streaming loads/stores are marked non-temporal so
+// they do not evict anything useful from the caches.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -40,28 +40,63 @@ __device__ __forceinline__ float bias_at(const void* b2, int b2_dtype, int64_t c
                              : static_cast<const float*>(b2)[c];
 }
 
+// b2[c .. c+3] widened to fp32 (c % 4 == 0).
+__device__ __forceinline__ f32x4 bias4(const void* b2, int b2_dtype, int64_t c)
+{
+    if (b2_dtype == kBF16) {
+        const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(b2) + c);
+        return f32x4{bf16_bits_to_f32(w.x & 0xffffu), bf16_bits_to_f32(w.x >> 16),
+                     bf16_bits_to_f32(w.y & 0xffffu), bf16_bits_to_f32(w.y >> 16)};
+    }
+    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(b2) + c);
+}
+
 // Vector path: D % 4 == 0, so the 4 elements of a vector share one row of b2's index space.
+// Each thread owns kVecs vectors spaced kBlock apart (so every load instruction of a wave is
+// one contiguous 1 KB run) and issues all T x kVecs loads before the first add: enough bytes
+// in flight per CU to cover HBM latency without a grid-stride loop.
+constexpr int kBlock = 256, kVecs = 4;
+
 template <int TT>
-__global__ __launch_bounds__(256) void partial_reduce_vec(PartialPtrs P, int T, const void* b2,
-                                                          int b2_dtype, float* Y, int64_t nvec,
-                                                          int64_t D)
+__global__ __launch_bounds__(kBlock) void partial_reduce_vec(PartialPtrs P, int T, const void* b2,
+                                                             int b2_dtype, float* Y, int64_t nvec,
+                                                             int64_t D, int64_t v0)
 {
     const int nt = TT > 0 ? TT : T;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
-        const int64_t e = v * 4;
-        f32x4 s = ld_nt(P.p[0] + e);
+    const int64_t base = v0 + (int64_t)blockIdx.x * (kBlock * kVecs) + threadIdx.x;
+    f32x4 s[kVecs];
 #pragma unroll
-        for (int r = 1; r < (TT > 0 ? TT : MLP_TP_MAX_REDUCE_T_INTERNAL); ++r) {
-            if (r >= nt) break;
-            s += ld_nt(P.p[r] + e);
-        }
-        if (b2) {
-            const int64_t c = e % D;
+    for (int u = 0; u < kVecs; ++u) {
+        const int64_t v = base + u * kBlock;
+        s[u] = v < nvec ? ld_nt(P.p[0] + v * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) s[q] += bias_at(b2, b2_dtype, c + q);
+    for (int r = 1; r < (TT > 0 ? TT : MLP_TP_MAX_REDUCE_T_INTERNAL); ++r) {
+        if (r >= nt) break;
+#pragma unroll
+        for (int u = 0; u < kVecs; ++u) {
+            const int64_t v = base + u * kBlock;
+            if (v < nvec) s[u] += ld_nt(P.p[r] + v * 4);
         }
-        st_nt(Y + e, s);
+    }
+    if (b2) {
+        // Column of the thread's first vector, then advanced by 4 kBlock elements per vector
+        // (one 64-bit remainder per thread, not per vector). The 4 bias values of a vector are
+        // contiguous and 8- or 16-byte aligned (b2 is 16-byte aligned and c % 4 == 0).
+        int64_t c = (base * 4) % D;
+#pragma unroll
+        for (int u = 0; u < kVecs; ++u) {
+            if (u > 0) {
+                c += 4 * kBlock;
+                while (c >= D) c -= D;
+            }
+            s[u] += bias4(b2, b2_dtype, c);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kVecs; ++u) {
+        const int64_t v = base + u * kBlock;
+        if (v < nvec) st_nt(Y + v * 4, s[u]);
     }
 }
 
@@ -86,18 +121,24 @@ void launch_partial_reduce(const float* const* P, int T, const void* b2, int b2_
     memset(&pp, 0, sizeof(pp));
     for (int r = 0; r < T; ++r) pp.p[r] = P[r];
     const int64_t n = N * D;
-    // Enough workgroups to keep every CU's memory pipeline full, then grid-stride.
+    // The element path grid-strides over at most this many workgroups.
     const int64_t max_groups = 256 * 16;
     if (D % 4 == 0) {
-        const int64_t nvec = n / 4;
-        const int64_t groups = ceil_div(nvec, 256) < max_groups ? ceil_div(nvec, 256) : max_groups;
-        const dim3 grid((uint32_t)groups), block(256);
-        switch (T) {
-        case 1: hipLaunchKernelGGL(partial_reduce_vec<1>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D); break;
-        case 2: hipLaunchKernelGGL(partial_reduce_vec<2>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D); break;
-        case 4: hipLaunchKernelGGL(partial_reduce_vec<4>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D); break;
-        case 8: hipLaunchKernelGGL(partial_reduce_vec<8>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D); break;
-        default: hipLaunchKernelGGL(partial_reduce_vec<0>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D); break;
+        // One launch per chunk of at most 2^30 workgroups (2^40 elements), so the grid size
+        // always fits; a single launch covers anything that fits in one GPU's memory.
+        const int64_t nvec = n / 4, per_group = (int64_t)kBlock * kVecs;
+        const int64_t max_launch = int64_t(1) << 30;
+        for (int64_t g0 = 0; g0 < ceil_div(nvec, per_group); g0 += max_launch) {
+            const int64_t groups = ceil_div(nvec, per_group) - g0;
+            const dim3 grid((uint32_t)(groups < max_launch ? groups : max_launch)), block(kBlock);
+            const int64_t v0 = g0 * per_group;
+            switch (T) {
+            case 1: hipLaunchKernelGGL(partial_reduce_vec<1>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D, v0); break;
+            case 2: hipLaunchKernelGGL(partial_reduce_vec<2>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D, v0); break;
+            case 4: hipLaunchKernelGGL(partial_reduce_vec<4>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D, v0); break;
+            case 8: hipLaunchKernelGGL(partial_reduce_vec<8>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D, v0); break;
+            default: hipLaunchKernelGGL(partial_reduce_vec<0>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D, v0); break;
+            }
         }
     } else {
         const int64_t groups = ceil_div(n, 256) < max_groups ? ceil_div(n, 256) : max_groups;

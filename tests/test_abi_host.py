@@ -216,3 +216,31 @@ def test_header_has_no_torch_or_hip_types():
     assert "torch" not in text.lower().replace("torch's", "")
     assert "hipStream_t" not in text.split("*/", 1)[1]  # streams travel as void*
     assert 'extern "C"' in text
+
+
+def _overlap(lib, ptrs, r=1, T=None, b2=None, Y=G, N=4, D=8, F=16, chunk=2, H=A, W2r=B):
+    import ctypes
+    T = len(ptrs) if T is None else T
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    return lib.mlp_tp_down_proj_overlap_tail(H, W2r, ctypes.cast(arr, ctypes.c_void_p), T, r, b2,
+                                             mt.F32, Y, N, D, F, mt.BF16, chunk, S, S)
+
+
+def test_overlap_tail_checks(lib):
+    """[U 3.8] the tail overlapped with the last shard's GEMM: host-side argument checks."""
+    import ctypes
+    assert lib.mlp_tp_down_proj_overlap_tail(A, B, None, 2, 1, None, mt.F32, G, 4, 8, 16,
+                                             mt.BF16, 2, S, S) == mt.E_NULL
+    assert _overlap(lib, [C, E], r=2) == mt.E_SHAPE                  # r outside [0, T)
+    assert _overlap(lib, [C, E], r=-1) == mt.E_SHAPE
+    assert _overlap(lib, [C, E], chunk=0) == mt.E_SHAPE
+    assert _overlap(lib, [C, E], N=1000, chunk=1) == mt.E_SHAPE      # more than 256 chunks
+    assert _overlap(lib, [C, None]) == mt.E_NULL
+    assert _overlap(lib, [C, E], F=15) == mt.E_INDIVISIBLE
+    assert _overlap(lib, [C, E + 4]) == mt.E_ALIGN
+    assert _overlap(lib, [C, E], Y=A) == mt.E_ALIAS                  # Y over H
+    assert _overlap(lib, [C, C + 64]) == mt.E_ALIAS                  # partials overlap
+    assert _overlap(lib, [C, E], Y=E + 16) == mt.E_ALIAS             # Y partly over P[1]
+    assert _overlap(lib, [C, E], Y=E, N=0) == mt.OK                  # exact alias, no rows
+    assert _overlap(lib, [C, E], N=0) == mt.OK
+    del ctypes
