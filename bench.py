@@ -32,6 +32,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "TP-shard MLP fwd TFLOP/s + % bf16 MFMA peak (D=8192, F/T=3584, N=4096)"
+ROWS = ("partial_reduce", "shard_bwd", "sum_dx", "gated_shard_fwd", "gpt3_layer",
+        "reduce_scatter_slice", "shard_count_sweep")
 
 
 def log(msg: str) -> None:
@@ -70,6 +72,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the extra per-row timings")
+    ap.add_argument("--rows", default="all",
+                    help="comma-separated subset of the extra rows to time: " + ", ".join(ROWS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -171,7 +175,12 @@ def main() -> int:
 
     rows = None
     if not args.no_rows:
-        rows = measure_rows(torch, mt, synth, workloads, dev, X, W1, b1, W2, H, w)
+        want = ROWS if args.rows == "all" else tuple(r for r in args.rows.split(",") if r)
+        unknown = [r for r in want if r not in ROWS]
+        if unknown:
+            log(f"unknown rows {unknown}; choose from {ROWS}")
+            return 2
+        rows = measure_rows(torch, mt, synth, workloads, dev, X, W1, b1, W2, H, w, want)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -217,11 +226,20 @@ def _time_loop(torch, fn, iters, warm=3):
     return a.elapsed_time(b) / iters
 
 
-def measure_rows(torch, mt, synth, workloads, dev, X, W1, b1, W2, H, w):
+def measure_rows(torch, mt, synth, workloads, dev, X, W1, b1, W2, H, w, want=ROWS):
     res = {}
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
+    if "partial_reduce" in want:
+        res.update(_row_partial_reduce(torch, mt, synth, workloads, dev, g))
+    if "shard_bwd" in want or "sum_dx" in want:
+        res.update(_rows_backward(torch, mt, synth, workloads, dev, g, X, W1, b1, W2, want))
+    res.update(measure_next_rows(torch, mt, synth, workloads, dev, g, want))
+    return res
 
+
+def _row_partial_reduce(torch, mt, synth, workloads, dev, g):
+    res = {}
     # Block tail of the GPT-3-175B layer: 8 fp32 partials [2048, 12288] + bf16 b2, once.
     w4 = workloads.GPT3_175B_T8
     parts = [torch.randn((w4.N, w4.D), generator=g, device=dev) for _ in range(w4.T)]
@@ -236,7 +254,11 @@ def measure_rows(torch, mt, synth, workloads, dev, X, W1, b1, W2, H, w):
                              "algorithmic_bytes": nbytes}
     log(f"[bench] reduce T=8 [2048,12288]: {ms:.4f} ms, {res['partial_reduce']['GB/s']} GB/s")
     del parts, Y
+    return res
 
+
+def _rows_backward(torch, mt, synth, workloads, dev, g, X, W1, b1, W2, want):
+    res = {}
     # Backward of the Llama shard (dY ~ N(0,1), seed 505).
     w5 = workloads.LLAMA70B_SHARD_T8_BWD
     N, D, F, T, Fs = w5.N, w5.D, w5.F, w5.T, w5.Fs
@@ -252,15 +274,18 @@ def measure_rows(torch, mt, synth, workloads, dev, X, W1, b1, W2, H, w):
     dX = torch.empty((N, D), device=dev)
     nb = mt.mlp_tp_shard_bwd_workspace_bytes(N, D, F, T)
     ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
-    ms = _time_loop(torch, lambda: mt.mlp_tp_shard_bwd(X, W1, W2, Z, Hz, dY, dZ, dW1, db1, dW2,
-                                                       dX, ws, nb, N, D, F, T, mt.BF16,
-                                                       w5.act), 10)
-    flop = 8.0 * N * D * Fs
-    res["shard_bwd"] = {"workload": w5.name, "ms": round(ms, 5),
-                        "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1),
-                        "frac_mfma": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    log(f"[bench] shard bwd: {ms:.4f} ms, {res['shard_bwd']['TFLOP/s']} TFLOP/s")
+    if "shard_bwd" in want:
+        ms = _time_loop(torch, lambda: mt.mlp_tp_shard_bwd(X, W1, W2, Z, Hz, dY, dZ, dW1, db1,
+                                                           dW2, dX, ws, nb, N, D, F, T, mt.BF16,
+                                                           w5.act), 10)
+        flop = 8.0 * N * D * Fs
+        res["shard_bwd"] = {"workload": w5.name, "ms": round(ms, 5),
+                            "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1),
+                            "frac_mfma": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench] shard bwd: {ms:.4f} ms, {res['shard_bwd']['TFLOP/s']} TFLOP/s")
     del dZ, dW1, dW2, db1, Z, Hz, P
+    if "sum_dx" not in want:
+        return res
 
     # Sum of the 8 dX partials [4096, 8192] (no bias).
     parts = [torch.randn((N, D), generator=g, device=dev) for _ in range(T)]
@@ -272,8 +297,6 @@ def measure_rows(torch, mt, synth, workloads, dev, X, W1, b1, W2, H, w):
                      "algorithmic_bytes": nbytes}
     log(f"[bench] sum dX T=8 [4096,8192]: {ms:.4f} ms, {res['sum_dx']['GB/s']} GB/s")
     del parts, dX, dY, ws
-
-    res.update(measure_next_rows(torch, mt, synth, workloads, dev, g))
     return res
 
 
@@ -281,12 +304,22 @@ def _randn_bf16(torch, shape, std, g, dev):
     return (torch.randn(shape, generator=g, device=dev) * std).to(torch.bfloat16)
 
 
-def measure_next_rows(torch, mt, synth, workloads, dev, g):
+def measure_next_rows(torch, mt, synth, workloads, dev, g, want=ROWS):
     """The gated shard, the three forms of the GPT-3-175B layer's block tail, one token slice of
     that tail, and the shard-count sweep at the Llama shape. Weights for these timing rows are
     drawn on the GPU (torch.randn, the workloads' distributions); parity is the tests' job."""
     res = {}
+    if "gated_shard_fwd" in want:
+        res.update(_row_gated(torch, mt, workloads, dev, g))
+    if "gpt3_layer" in want or "reduce_scatter_slice" in want:
+        res.update(_rows_gpt3_layer(torch, mt, workloads, dev, g, want))
+    if "shard_count_sweep" in want:
+        res.update(_row_t_sweep(torch, mt, workloads, dev, g))
+    return res
 
+
+def _row_gated(torch, mt, workloads, dev, g):
+    res = {}
     # Gated (SwiGLU) shard of the Llama-3-70B FFN: gate and up in one dual GEMM, then down.
     w = workloads.LLAMA70B_SWIGLU_SHARD_T8
     N, D, F, T, Fs = w.N, w.D, w.F, w.T, w.Fs
@@ -303,7 +336,11 @@ def measure_next_rows(torch, mt, synth, workloads, dev, g):
                               "frac_mfma": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     log(f"[bench] gated shard fwd: {ms:.4f} ms, {res['gated_shard_fwd']['TFLOP/s']} TFLOP/s")
     del X, Wg, Wu, W2, H, P
+    return res
 
+
+def _rows_gpt3_layer(torch, mt, workloads, dev, g, want):
+    res = {}
     # The GPT-3-175B MLP layer on one GPU: 8 shards of F/T = 6144 in sequence and the tail,
     #   separate: 8 fp32 partials, then the T-way reduce with b2;
     #   accumulate: each down-projection adds into one buffer seeded with b2;
@@ -344,14 +381,19 @@ def measure_next_rows(torch, mt, synth, workloads, dev, g):
                                          mt.BF16, chunk, tail_stream=side)
 
     flop = 4.0 * N * D * F  # all 8 shards' GEMMs
-    layer = {"workload": w.name, "flop": flop, "tail_chunk_rows": chunk}
-    for name, fn in (("separate", separate), ("accumulate", accumulate),
-                     ("overlapped", overlapped)):
-        ms = _time_loop(torch, fn, 10)
-        layer[name] = {"ms": round(ms, 4), "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1)}
-        log(f"[bench] gpt3 layer ({name}): {ms:.4f} ms")
-    res["gpt3_layer"] = layer
+    if "gpt3_layer" in want:
+        layer = {"workload": w.name, "flop": flop, "tail_chunk_rows": chunk}
+        for name, fn in (("separate", separate), ("accumulate", accumulate),
+                         ("overlapped", overlapped)):
+            ms = _time_loop(torch, fn, 10)
+            layer[name] = {"ms": round(ms, 4), "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1)}
+            log(f"[bench] gpt3 layer ({name}): {ms:.4f} ms")
+        res["gpt3_layer"] = layer
+    else:
+        separate()  # the partials the slice reduces
 
+    if "reduce_scatter_slice" not in want:
+        return res
     # One token slice of that tail (reduce-scatter layout): rank 0's N / T rows.
     row0, rows = mt.mlp_tp_token_slice(N, T, 0)
     Yr = torch.empty((rows, D), device=dev)
@@ -364,7 +406,11 @@ def measure_next_rows(torch, mt, synth, workloads, dev, g):
                                    "algorithmic_bytes": nbytes}
     log(f"[bench] reduce-scatter slice: {ms:.4f} ms, {res['reduce_scatter_slice']['GB/s']} GB/s")
     del X, W1s, b1s, W2s, H, parts, Y, Yr
+    return res
 
+
+def _row_t_sweep(torch, mt, workloads, dev, g):
+    res = {}
     # Shard count sweep at the Llama shape: one rank's forward for T = 1, 2, 4, 8.
     w = workloads.LLAMA70B_SHARD_T8
     N, D, F = w.N, w.D, w.F

@@ -19,6 +19,7 @@ using DefaultTile = MfmaTile<128, 128, 2, 2>;
 using DmaTile256x256 = DmaTile<256, 256, 4, 2>;
 using DmaTile256x224 = DmaTile<256, 224, 4, 2>;
 using DmaTile224x256 = DmaTile<224, 256, 2, 4>;
+using DmaTile256x192 = DmaTile<256, 192, 4, 2>;
 
 int compute_units();  // of the current device, queried once
 
@@ -76,15 +77,21 @@ inline void run_bf16(const void* A, const void* B, int64_t M, int64_t N, int64_t
                      int64_t ldb, Epi epi, hipStream_t s)
 {
     if (dma_eligible(A_KC, B_KC, M, N, K, lda, ldb)) {
-        const int64_t c256 = tile_cost(M, N, 256, 256);
-        const int64_t c224n = (N % 224 == 0) ? tile_cost(M, N, 256, 224) : INT64_MAX;
-        const int64_t c224m = (M % 224 == 0) ? tile_cost(M, N, 224, 256) : INT64_MAX;
-        if (c224n < c256 && c224n <= c224m)
-            run_dma<DmaTile256x224, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s);
-        else if (c224m < c256)
-            run_dma<DmaTile224x256, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s);
-        else
-            run_dma<DmaTile256x256, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s);
+        // Candidates in order of preference (larger tiles first); the first of the lowest cost
+        // wins. The narrower tiles only where they divide the extent exactly.
+        const int64_t cost[4] = {tile_cost(M, N, 256, 256),
+                                 (N % 224 == 0) ? tile_cost(M, N, 256, 224) : INT64_MAX,
+                                 (M % 224 == 0) ? tile_cost(M, N, 224, 256) : INT64_MAX,
+                                 (N % 192 == 0) ? tile_cost(M, N, 256, 192) : INT64_MAX};
+        int best = 0;
+        for (int c = 1; c < 4; ++c)
+            if (cost[c] < cost[best]) best = c;
+        switch (best) {
+        case 1: run_dma<DmaTile256x224, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
+        case 2: run_dma<DmaTile224x256, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
+        case 3: run_dma<DmaTile256x192, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
+        default: run_dma<DmaTile256x256, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
+        }
     } else
         run_mfma<DefaultTile, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s);
 }

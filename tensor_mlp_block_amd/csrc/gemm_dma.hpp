@@ -53,11 +53,17 @@ __device__ __forceinline__ int kc_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) 
 //   * ROWS = 224: a 448-byte row pitch already spreads 4 consecutive rows over distinct banks;
 //     only rows 8 apart collide, so flip chunk bit 1 with bit 3 of k (stays inside the row's
 //     28 chunks, since it permutes within aligned groups of 4).
+//   * ROWS = 192: a 384-byte pitch puts odd k rows half a bank period from even ones, so rows
+//     2 apart collide; bit 1 of k flips chunk bit 1 and bit 3 of k chunk bit 2, which gives the
+//     8 rows one half-wave reads 8 distinct bank groups and stays inside aligned groups of 8
+//     of the row's 24 chunks.
 template <int ROWS>
 __device__ __forceinline__ int mc_swz(int k)
 {
     if constexpr (ROWS == 224)
         return ((k >> 3) & 1) << 1;
+    else if constexpr (ROWS == 192)
+        return (((k >> 1) & 1) << 1) | (((k >> 3) & 1) << 2);
     else if constexpr (ROWS >= 128)
         return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
     else

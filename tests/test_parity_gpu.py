@@ -232,6 +232,8 @@ RAGGED = [
              bias=False),
     # widths that are multiples of 224: the 256x224 and 224x256 tiles, with a ragged token tail
     Workload("tile224_n300_d448_f896_t2", 300, 448, 896, 2, "gelu_tanh", "bf16", 7008, "normal"),
+    # widths that are multiples of 192: the 256x192 tile (both weight layouts in the backward)
+    Workload("tile192_n300_d384_f768_t2", 300, 384, 768, 2, "gelu_tanh", "bf16", 7009, "normal"),
 ]
 
 
