@@ -6,6 +6,7 @@
  *   [C] charliedreemur.github.io, "TP:Column / Row Parallel Linear 怎么切? MLP 和 attention 怎么切?"
  *   [U] unpurerationalist.github.io, "LLM Systems 16: Model Parallel Training"
  *   [J] jwzheng96.github.io, "张量并行 TP 与列并行 / 行并行的实现" (Megatron-LM tutorial ch. 7)
+ *   [F] 5688vip.com, "4、张量并行原理：张量切分方式（行并行、列并行）…"
  *
  * The method. An MLP H = phi(X W1 + b1), Y = H W2 + b2 [Z 01] is split over T ranks: W1 by
  * columns and W2 by the matching rows [Z 02], [U 3.2], [J 7.2]. Rank r (Fs = F / T hidden
@@ -169,9 +170,10 @@ int mlp_tp_down_proj_accumulate(const void* H, const void* W2r, float* P, int64_
                                 int64_t F, int32_t T, int32_t dtype, void* stream);
 
 /*
- * Row-parallel down-projection of rank r overlapped with the block tail [U 3.8]: on one GPU,
- * the last shard's GEMM and the reduction of the finished token rows run at the same time,
- * the local form of overlapping the tail's all-reduce with the rest of the layer. The token
+ * Row-parallel down-projection of rank r overlapped with the block tail [F 4.4.2], [F 4.4.3]:
+ * on one GPU, the last shard's GEMM and the reduction of the finished token rows run at the
+ * same time, the local form of cutting the tail's all-reduce into chunks, each sent as soon as
+ * it is computed, on a stream of its own. The token
  * rows are cut into chunks of chunk_rows:
  *     P[r][chunk]  = H[chunk] . W2r                                   on `stream`;
  *     Y[chunk]     = (((P[0] + P[1]) + ...) + P[T-1])[chunk] + b2      on `tail_stream`,

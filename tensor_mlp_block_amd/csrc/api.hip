@@ -7,6 +7,7 @@
 // Pages cited, as [tag section]:
 //   [Z] zwjcode.cn, "一层 MLP 太宽而放不下时怎样切？列并行、行并行与块尾归约"
 //   [U] unpurerationalist.github.io, "LLM Systems 16: Model Parallel Training"
+//   [F] 5688vip.com, "4、张量并行原理：张量切分方式（行并行、列并行）…"
 #include "../../include/mlp_tp.h"
 #include "launch.hpp"
 
@@ -308,6 +309,7 @@ int mlp_tp_down_proj_overlap_tail(const void* H, const void* W2r, const float* c
         for (int32_t s = 0; s < T; ++s) Ps[s] = P[s] + row0 * D;
         mlptp::launch_partial_reduce(Ps, T, b2, b2_dtype, Y + row0 * D, rows, D, s1);
     }
+    // Chunked tail on its own stream, each chunk started as soon as it is computed [F 4.4.2].
     // Join: work queued on the compute stream after this call sees Y complete.
     if (hipEventRecord(ev[chunks], s1) != hipSuccess) return MLP_TP_E_HIP;
     if (hipStreamWaitEvent(s0, ev[chunks], 0) != hipSuccess) return MLP_TP_E_HIP;

@@ -227,7 +227,7 @@ def _overlap(lib, ptrs, r=1, T=None, b2=None, Y=G, N=4, D=8, F=16, chunk=2, H=A,
 
 
 def test_overlap_tail_checks(lib):
-    """[U 3.8] the tail overlapped with the last shard's GEMM: host-side argument checks."""
+    """[F 4.4.2] the tail overlapped with the last shard's GEMM: host-side argument checks."""
     import ctypes
     assert lib.mlp_tp_down_proj_overlap_tail(A, B, None, 2, 1, None, mt.F32, G, 4, 8, 16,
                                              mt.BF16, 2, S, S) == mt.E_NULL

@@ -6,6 +6,7 @@ Pages cited:
   [Z] zwjcode.cn, "一层 MLP 太宽而放不下时怎样切？列并行、行并行与块尾归约"
   [U] unpurerationalist.github.io, "LLM Systems 16: Model Parallel Training"
   [C] charliedreemur.github.io, "TP:Column / Row Parallel Linear 怎么切? MLP 和 attention 怎么切?"
+  [F] 5688vip.com, "4、张量并行原理：张量切分方式（行并行、列并行）…"
 """
 import sys
 
@@ -94,7 +95,7 @@ OVERLAP = [
 @pytest.mark.parametrize("two_streams", [True, False])
 def test_overlapped_tail_matches_oracle_and_plain_tail(w, chunk, two_streams):
     """Shards 0 .. T-2 computed as usual; the last shard's down-projection runs in token chunks
-    with the block tail of each finished chunk on a second stream [U 3.8]. Y must equal the
+    with the block tail of each finished chunk on a second stream [F 4.4.2]. Y must equal the
     plain path (the same kernels on the same rows, bit for bit) and the oracle [Z 05]."""
     _say(f"  workload {w.name} chunk {chunk} two_streams {two_streams}")
     Xc = synth.gen_X(w)
