@@ -8,6 +8,7 @@ forward shard through the C ABI: the column-parallel up-projection with fused bi
 `value` is the forward's GEMM work (4 N D F/T flops) per second.
 
 Also measured in the same run, each over its own timed loop (reported under "rows"): the
+same forward step with operands that are not in any cache (three copies in rotation), the
 block-tail reduction of 8 fp32 partials [2048, 12288] with b2 (the GPT-3-175B layer's tail),
 the shard backward at the Llama shape, the sum of 8 dX partials [4096, 8192], the gated
 (SwiGLU) shard forward, the whole GPT-3-175B layer on one GPU with its tail as separate
@@ -32,8 +33,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "TP-shard MLP fwd TFLOP/s + % bf16 MFMA peak (D=8192, F/T=3584, N=4096)"
-ROWS = ("partial_reduce", "shard_bwd", "sum_dx", "gated_shard_fwd", "gpt3_layer",
-        "reduce_scatter_slice", "shard_count_sweep")
+ROWS = ("fwd_cold_operands", "partial_reduce", "shard_bwd", "sum_dx", "gated_shard_fwd",
+        "gpt3_layer", "reduce_scatter_slice", "shard_count_sweep")
 
 
 def log(msg: str) -> None:
@@ -230,12 +231,51 @@ def measure_rows(torch, mt, synth, workloads, dev, X, W1, b1, W2, H, w, want=ROW
     res = {}
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
+    if "fwd_cold_operands" in want:
+        res.update(_row_cold(torch, mt, dev, X, W1, b1, W2, H, w))
     if "partial_reduce" in want:
         res.update(_row_partial_reduce(torch, mt, synth, workloads, dev, g))
     if "shard_bwd" in want or "sum_dx" in want:
         res.update(_rows_backward(torch, mt, synth, workloads, dev, g, X, W1, b1, W2, want))
     res.update(measure_next_rows(torch, mt, synth, workloads, dev, g, want))
     return res
+
+
+def _row_cold(torch, mt, dev, X, W1, b1, W2, H, w, copies=3):
+    """The headline step with operands that are not in any cache: the steps rotate through
+    `copies` separate copies of X, W1, b1, W2 (together larger than the 256 MB last-level cache),
+    so each step reads its operands from HBM. The headline itself repeats one set of operands,
+    which then stays in that cache from step to step."""
+    N, D, F, T, Fs = w.N, w.D, w.F, w.T, w.Fs
+    sets = [(X, W1, b1, W2)] + [(X.clone(), W1.clone(), b1.clone(), W2.clone())
+                                for _ in range(copies - 1)]
+    P = torch.empty((N, D), dtype=torch.float32, device=dev)
+    steps = 10 * copies
+    s = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(2 * copies):
+        Xi, W1i, b1i, W2i = sets[i % copies]
+        mt.mlp_tp_up_proj(Xi, W1i, b1i, None, H, N, D, F, T, mt.BF16, w.act)
+        mt.mlp_tp_down_proj(H, W2i, P, N, D, F, T, mt.BF16)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        Xi, W1i, b1i, W2i = sets[i % copies]
+        ev[i][0].record(s)
+        mt.mlp_tp_up_proj(Xi, W1i, b1i, None, H, N, D, F, T, mt.BF16, w.act)
+        ev[i][1].record(s)
+        mt.mlp_tp_down_proj(H, W2i, P, N, D, F, T, mt.BF16)
+        ev[i][2].record(s)
+    torch.cuda.synchronize()
+    up = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    down = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    flop = 4.0 * N * D * Fs
+    out = {"copies": copies, "up_ms": round(up, 5), "down_ms": round(down, 5),
+           "TFLOP/s": round(flop / ((up + down) * 1e-3) / 1e12, 1),
+           "frac_mfma": round(flop / ((up + down) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    log(f"[bench] forward with cold operands: up {up:.4f} ms down {down:.4f} ms, "
+        f"{out['TFLOP/s']} TFLOP/s")
+    del sets, P
+    return {"fwd_cold_operands": out}
 
 
 def _row_partial_reduce(torch, mt, synth, workloads, dev, g):

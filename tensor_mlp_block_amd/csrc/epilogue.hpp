@@ -138,7 +138,14 @@ struct EpiStore {
                                           int64_t M, int64_t N) const
     {
         const int n = valid4(row, col, M, N);
-        if (n) store4(C + row * ldc + col, v, n, vec);
+        if (!n) return;
+        // fp32 results (a partial, a gradient) are written once and read later by another
+        // kernel, usually after far more other traffic than the caches hold: stream them past
+        // the caches, so they do not evict operands that are read again.
+        if (std::is_same<T, float>::value && vec && n == 4)
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + row * ldc + col));
+        else
+            store4(C + row * ldc + col, v, n, vec);
     }
     __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 v, int64_t M,
                                                int64_t N) const
