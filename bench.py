@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "TP-shard MLP fwd TFLOP/s + % bf16 MFMA peak (D=8192, F/T=3584, N=4096)"
 ROWS = ("fwd_cold_operands", "partial_reduce", "shard_bwd", "sum_dx", "gated_shard_fwd",
-        "gpt3_layer", "reduce_scatter_slice", "shard_count_sweep")
+        "gated_shard_bwd", "gpt3_layer", "reduce_scatter_slice", "shard_count_sweep")
 
 
 def log(msg: str) -> None:
@@ -349,8 +349,8 @@ def measure_next_rows(torch, mt, synth, workloads, dev, g, want=ROWS):
     that tail, and the shard-count sweep at the Llama shape. Weights for these timing rows are
     drawn on the GPU (torch.randn, the workloads' distributions); parity is the tests' job."""
     res = {}
-    if "gated_shard_fwd" in want:
-        res.update(_row_gated(torch, mt, workloads, dev, g))
+    if "gated_shard_fwd" in want or "gated_shard_bwd" in want:
+        res.update(_row_gated(torch, mt, workloads, dev, g, want))
     if "gpt3_layer" in want or "reduce_scatter_slice" in want:
         res.update(_rows_gpt3_layer(torch, mt, workloads, dev, g, want))
     if "shard_count_sweep" in want:
@@ -358,9 +358,11 @@ def measure_next_rows(torch, mt, synth, workloads, dev, g, want=ROWS):
     return res
 
 
-def _row_gated(torch, mt, workloads, dev, g):
+def _row_gated(torch, mt, workloads, dev, g, want):
     res = {}
-    # Gated (SwiGLU) shard of the Llama-3-70B FFN: gate and up in one dual GEMM, then down.
+    # Gated (SwiGLU) shard of the Llama-3-70B FFN: gate and up in one dual GEMM, then down; its
+    # backward: dG and dU from one GEMM with the product rule in the epilogue, three weight
+    # gradients, and dX as two GEMMs into one fp32 buffer.
     w = workloads.LLAMA70B_SWIGLU_SHARD_T8
     N, D, F, T, Fs = w.N, w.D, w.F, w.T, w.Fs
     X = _randn_bf16(torch, (N, D), 1.0, g, dev)
@@ -368,13 +370,33 @@ def _row_gated(torch, mt, workloads, dev, g):
     W2 = _randn_bf16(torch, (Fs, D), 0.02, g, dev)
     H = torch.empty((N, Fs), dtype=torch.bfloat16, device=dev)
     P = torch.empty((N, D), device=dev)
-    ms = _time_loop(torch, lambda: mt.mlp_tp_swiglu_shard_fwd(X, Wg, Wu, W2, None, None, H, P, N,
-                                                              D, F, T, mt.BF16), 20)
-    flop = 6.0 * N * D * Fs
-    res["gated_shard_fwd"] = {"workload": w.name, "ms": round(ms, 5),
-                              "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1),
-                              "frac_mfma": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    log(f"[bench] gated shard fwd: {ms:.4f} ms, {res['gated_shard_fwd']['TFLOP/s']} TFLOP/s")
+    if "gated_shard_fwd" in want:
+        ms = _time_loop(torch, lambda: mt.mlp_tp_swiglu_shard_fwd(X, Wg, Wu, W2, None, None, H, P,
+                                                                  N, D, F, T, mt.BF16), 20)
+        flop = 6.0 * N * D * Fs
+        res["gated_shard_fwd"] = {"workload": w.name, "ms": round(ms, 5),
+                                  "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1),
+                                  "frac_mfma": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                                     4)}
+        log(f"[bench] gated shard fwd: {ms:.4f} ms, {res['gated_shard_fwd']['TFLOP/s']} TFLOP/s")
+    if "gated_shard_bwd" in want:
+        G = torch.empty((N, Fs), dtype=torch.bfloat16, device=dev)
+        U = torch.empty_like(G)
+        mt.mlp_tp_swiglu_shard_fwd(X, Wg, Wu, W2, G, U, H, P, N, D, F, T, mt.BF16)
+        dY = torch.randn((N, D), generator=g, device=dev).to(torch.bfloat16)
+        dG, dU = torch.empty_like(G), torch.empty_like(G)
+        dWg, dWu = torch.empty((D, Fs), device=dev), torch.empty((D, Fs), device=dev)
+        dW2 = torch.empty((Fs, D), device=dev)
+        dX = P  # the forward's partial buffer, reused
+        ms = _time_loop(torch, lambda: mt.mlp_tp_swiglu_shard_bwd(
+            X, Wg, Wu, W2, G, U, H, dY, dG, dU, dWg, dWu, dW2, dX, N, D, F, T, mt.BF16), 10)
+        flop = 12.0 * N * D * Fs
+        res["gated_shard_bwd"] = {"workload": w.name, "ms": round(ms, 5),
+                                  "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1),
+                                  "frac_mfma": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                                     4)}
+        log(f"[bench] gated shard bwd: {ms:.4f} ms, {res['gated_shard_bwd']['TFLOP/s']} TFLOP/s")
+        del G, U, dY, dG, dU, dWg, dWu, dW2, dX
     del X, Wg, Wu, W2, H, P
     return res
 

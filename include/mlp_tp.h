@@ -258,6 +258,29 @@ int mlp_tp_shard_bwd(const void* X, const void* W1r, const void* W2r, const void
                      int64_t N, int64_t D, int64_t F, int32_t T, int32_t dtype, int32_t act,
                      void* stream);
 
+/*
+ * Backward of one rank's gated (SwiGLU) shard [Z 08] for the upstream gradient dY, by the
+ * same rules as mlp_tp_shard_bwd [Z 06], [U 3.6.1] with the product rule through
+ * H = SiLU(G) * U:
+ *     dH   = dY . W2r^T                    (local, as in the plain shard)
+ *     dU   = dH (.) SiLU(G)                dG = dH (.) U (.) SiLU'(G),
+ *                                          SiLU'(g) = s (1 + g (1 - s)), s = sigmoid(g)
+ *     dW2r = H^T . dY      dWgr = X^T . dG      dWur = X^T . dU
+ *     dXr  = dG . Wgr^T + dU . Wur^T       (this rank's partial of dX)
+ *   Inputs (dtype): X [N, D], Wgr, Wur [D, Fs], W2r [Fs, D], G, U and H [N, Fs] as stored by
+ *   mlp_tp_swiglu_shard_fwd, dY [N, D].
+ *   Outputs: dG, dU [N, Fs] dtype (rounded once when stored; the weight and input gradients are
+ *   formed from the stored values); dWgr, dWur [D, Fs], dW2r [Fs, D] and dXr [N, D], float.
+ *   No workspace: the gated form has no bias, so no column sum.
+ * Errors: E_NULL (any pointer), E_SHAPE, E_INDIVISIBLE, E_DTYPE, E_ALIGN, E_ALIAS (any output
+ * overlapping an input or another output), E_HIP.
+ */
+int mlp_tp_swiglu_shard_bwd(const void* X, const void* Wgr, const void* Wur, const void* W2r,
+                            const void* G, const void* U, const void* H, const void* dY, void* dG,
+                            void* dU, float* dWgr, float* dWur, float* dW2r, float* dXr,
+                            int64_t N, int64_t D, int64_t F, int32_t T, int32_t dtype,
+                            void* stream);
+
 /* Static description of a return code; never NULL. */
 const char* mlp_tp_strerror(int code);
 

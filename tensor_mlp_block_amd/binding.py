@@ -63,6 +63,7 @@ def load() -> ctypes.CDLL:
                                   ctypes.c_int),
         "mlp_tp_swiglu_shard_fwd": ([vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
                                      vp], ctypes.c_int),
+        "mlp_tp_swiglu_shard_bwd": ([vp] * 14 + [i64, i64, i64, i32, i32, vp], ctypes.c_int),
         "mlp_tp_strerror": ([ctypes.c_int], ctypes.c_char_p),
     }
     for name, (args, res) in sigs.items():
@@ -201,6 +202,15 @@ def mlp_tp_shard_bwd(X, W1r, W2r, Z, H, dY, dZ, dW1r, db1r, dW2r, dXr, workspace
                                  _ptr(workspace), int(workspace_bytes), N, D, F, T, dtype,
                                  _act(act), _stream(stream))
     return _check(rc, "mlp_tp_shard_bwd")
+
+
+def mlp_tp_swiglu_shard_bwd(X, Wgr, Wur, W2r, G, U, H, dY, dG, dU, dWgr, dWur, dW2r, dXr, N, D, F,
+                            T, dtype, stream=None):
+    rc = load().mlp_tp_swiglu_shard_bwd(_ptr(X), _ptr(Wgr), _ptr(Wur), _ptr(W2r), _ptr(G), _ptr(U),
+                                        _ptr(H), _ptr(dY), _ptr(dG), _ptr(dU), _ptr(dWgr),
+                                        _ptr(dWur), _ptr(dW2r), _ptr(dXr), N, D, F, T, dtype,
+                                        _stream(stream))
+    return _check(rc, "mlp_tp_swiglu_shard_bwd")
 
 
 def mlp_tp_strerror(code: int) -> str:

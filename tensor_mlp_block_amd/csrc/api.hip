@@ -405,6 +405,50 @@ int mlp_tp_shard_bwd(const void* X, const void* W1r, const void* W2r, const void
     return launch_status();
 }
 
+int mlp_tp_swiglu_shard_bwd(const void* X, const void* Wgr, const void* Wur, const void* W2r,
+                            const void* G, const void* U, const void* H, const void* dY, void* dG,
+                            void* dU, float* dWgr, float* dWur, float* dW2r, float* dXr,
+                            int64_t N, int64_t D, int64_t F, int32_t T, int32_t dtype,
+                            void* stream)
+{
+    if (!X || !Wgr || !Wur || !W2r || !G || !U || !H || !dY || !dG || !dU || !dWgr || !dWur ||
+        !dW2r || !dXr)
+        return MLP_TP_E_NULL;
+    if (int rc = check_shard_shape(N, D, F, T)) return rc;
+    if (!dtype_ok(dtype)) return MLP_TP_E_DTYPE;
+    if (int rc = all_aligned({X, Wgr, Wur, W2r, G, U, H, dY, dG, dU, dWgr, dWur, dW2r, dXr}))
+        return rc;
+    const int64_t es = elem_size(dtype), Fs = F / T;
+    if (int rc = disjoint({{dG, N * Fs * es}, {dU, N * Fs * es}, {dWgr, D * Fs * 4},
+                           {dWur, D * Fs * 4}, {dW2r, Fs * D * 4}, {dXr, N * D * 4}},
+                          {{X, N * D * es}, {Wgr, D * Fs * es}, {Wur, D * Fs * es},
+                           {W2r, Fs * D * es}, {G, N * Fs * es}, {U, N * Fs * es},
+                           {H, N * Fs * es}, {dY, N * D * es}}))
+        return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // With N == 0 tokens the weight gradients are empty sums: the K = 0 products write zeros.
+    if (N > 0) {
+        // dG, dU from dH = dY W2r^T and the product rule through SiLU(G) * U  [Z 08]
+        mlptp::launch_swiglu_bwd_dgu(dY, W2r, G, U, dG, dU, N, D, Fs, dtype, s);
+        if (int rc = launch_status()) return rc;
+    }
+    // dW2r = H^T dY   [U 3.6.1]
+    mlptp::launch_wgrad(H, dY, dW2r, Fs, D, N, Fs, D, dtype, s);
+    if (int rc = launch_status()) return rc;
+    // dWgr = X^T dG, dWur = X^T dU
+    mlptp::launch_wgrad(X, dG, dWgr, D, Fs, N, D, Fs, dtype, s);
+    if (int rc = launch_status()) return rc;
+    mlptp::launch_wgrad(X, dU, dWur, D, Fs, N, D, Fs, dtype, s);
+    if (int rc = launch_status()) return rc;
+    if (N > 0) {
+        // dXr = dG Wgr^T + dU Wur^T: the two input-gradient terms of the gated shard
+        mlptp::launch_dx(dG, Wgr, dXr, N, D, Fs, dtype, s);
+        if (int rc = launch_status()) return rc;
+        mlptp::launch_dx_accumulate(dU, Wur, dXr, N, D, Fs, dtype, s);
+    }
+    return launch_status();
+}
+
 const char* mlp_tp_strerror(int code)
 {
     switch (code) {

@@ -30,6 +30,24 @@ void launch_bwd_dz(const void* dY, const void* W2r, const void* Z, void* dZ, int
     });
 }
 
+// Gated form [Z 08]: the same dH = dY W2^(r)^T product, with the product rule through
+// H = SiLU(G) * U in its epilogue, so dG and dU each take one HBM write and G, U one read.
+void launch_swiglu_bwd_dgu(const void* dY, const void* W2r, const void* G, const void* U, void* dG,
+                           void* dU, int64_t N, int64_t D, int64_t Fs, int dtype, hipStream_t s)
+{
+    const int vec = (Fs % 4 == 0);
+    if (dtype == kBF16) {
+        EpiSwiGLUGrad<uint16_t> epi{static_cast<const uint16_t*>(G),
+                                    static_cast<const uint16_t*>(U), static_cast<uint16_t*>(dG),
+                                    static_cast<uint16_t*>(dU), Fs, vec};
+        run_bf16<true, true>(dY, W2r, N, Fs, D, D, D, epi, s);
+    } else {
+        EpiSwiGLUGrad<float> epi{static_cast<const float*>(G), static_cast<const float*>(U),
+                                 static_cast<float*>(dG), static_cast<float*>(dU), Fs, vec};
+        run_simt<true, true>(dY, W2r, N, Fs, D, D, D, epi, s);
+    }
+}
+
 // Local weight gradients [Z 06], [U 3.6.1]: C = A^T B, both operands stored token-major
 // ([K, M] and [K, N]), so both are transposed into LDS.
 void launch_wgrad(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
@@ -49,6 +67,18 @@ void launch_dx(const void* dZ, const void* W1r, float* dX, int64_t N, int64_t D,
                int dtype, hipStream_t s)
 {
     EpiStoreF32 epi{dX, D, (int)(D % 4 == 0)};
+    if (dtype == kBF16)
+        run_bf16<true, true>(dZ, W1r, N, D, Fs, Fs, Fs, epi, s);
+    else
+        run_simt<true, true>(dZ, W1r, N, D, Fs, Fs, Fs, epi, s);
+}
+
+// dX^(r) += dZ W1^(r)^T: the gated form's second input-gradient term, dU Wu^(r)^T added to
+// dG Wg^(r)^T [Z 08].
+void launch_dx_accumulate(const void* dZ, const void* W1r, float* dX, int64_t N, int64_t D,
+                          int64_t Fs, int dtype, hipStream_t s)
+{
+    EpiAccumF32 epi{dX, D, (int)(D % 4 == 0)};
     if (dtype == kBF16)
         run_bf16<true, true>(dZ, W1r, N, D, Fs, Fs, Fs, epi, s);
     else

@@ -330,4 +330,53 @@ struct EpiGateMul {
     }
 };
 
+// Gated MLP backward [Z 08], through H = SiLU(g) * u by the product rule: the GEMM produced
+// dh = dY W2^(r)^T for four columns; with s = sigmoid(g), dU = dh * SiLU(g) and
+// dG = dh * u * SiLU'(g), where SiLU'(g) = s * (1 + g * (1 - s)). G and U are the stored
+// pre-activations of the forward; dG and dU are written in the same dtype.
+template <class T>
+struct EpiSwiGLUGrad {
+    const T* G;  // [M, N]
+    const T* U;  // [M, N]
+    T* dG;       // [M, N]
+    T* dU;       // [M, N]
+    int64_t ldc;
+    int vec;
+    using ColData = NoData;
+    struct ElemData {
+        Staged4<T> g, u;
+    };
+    static constexpr bool kColData = false, kElemData = true;
+    __device__ __forceinline__ ColData col_load(int64_t, int64_t) const { return {}; }
+    __device__ __forceinline__ ElemData elem_load(int64_t row, int64_t col, int64_t M,
+                                                  int64_t N) const
+    {
+        const int n = valid4(row, col, M, N);
+        if (!n) return {Staged4<T>::load(G, 0, false), Staged4<T>::load(U, 0, false)};
+        return {Staged4<T>::load(G + row * ldc + col, n, vec),
+                Staged4<T>::load(U + row * ldc + col, n, vec)};
+    }
+    __device__ __forceinline__ void apply(int64_t row, int64_t col, f32x4 dh, ColData,
+                                          ElemData gu, int64_t M, int64_t N) const
+    {
+        const int n = valid4(row, col, M, N);
+        if (!n) return;
+        const f32x4 g = gu.g.get(), u = gu.u.get();
+        f32x4 dg, du;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float s = sigmoidf_(g[e]);
+            du[e] = dh[e] * (g[e] * s);
+            dg[e] = dh[e] * u[e] * (s * (1.0f + g[e] * (1.0f - s)));
+        }
+        store4(dG + row * ldc + col, dg, n, vec);
+        store4(dU + row * ldc + col, du, n, vec);
+    }
+    __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 dh, int64_t M,
+                                               int64_t N) const
+    {
+        apply(row, col, dh, {}, elem_load(row, col, M, N), M, N);
+    }
+};
+
 }  // namespace mlptp

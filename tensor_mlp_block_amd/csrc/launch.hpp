@@ -34,6 +34,11 @@ void launch_swiglu_up(const void* X, const void* Wg, const void* Wu, void* G, vo
 void launch_bwd_dz(const void* dY, const void* W2r, const void* Z, void* dZ, int64_t N, int64_t D,
                    int64_t Fs, int dtype, int act, hipStream_t s);
 
+// Gated backward through the activation: dH = dY W2r^T, then dG = dH * U * SiLU'(G) and
+// dU = dH * SiLU(G). dY [N, D], W2r [Fs, D], G/U/dG/dU [N, Fs].
+void launch_swiglu_bwd_dgu(const void* dY, const void* W2r, const void* G, const void* U, void* dG,
+                           void* dU, int64_t N, int64_t D, int64_t Fs, int dtype, hipStream_t s);
+
 // C [M, N] fp32 = A^T B with A stored [K, M] (lda) and B stored [K, N] (ldb): the weight
 // gradients dW2r = H^T dY and dW1r = X^T dZ.
 void launch_wgrad(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K,
@@ -42,6 +47,10 @@ void launch_wgrad(const void* A, const void* B, float* C, int64_t M, int64_t N, 
 // dX = dZ W1r^T. dZ [N, Fs], W1r [D, Fs], dX [N, D] fp32.
 void launch_dx(const void* dZ, const void* W1r, float* dX, int64_t N, int64_t D, int64_t Fs,
                int dtype, hipStream_t s);
+
+// dX += dZ W1r^T (fp32 accumulation into an existing dX).
+void launch_dx_accumulate(const void* dZ, const void* W1r, float* dX, int64_t N, int64_t D,
+                          int64_t Fs, int dtype, hipStream_t s);
 
 // db1 [Fs] = column sums of dZ [N, Fs], deterministic two-pass through `ws`.
 int64_t colsum_workspace_bytes(int64_t N, int64_t Fs);

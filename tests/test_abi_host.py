@@ -210,6 +210,33 @@ def test_shard_bwd_argument_checks(lib):
     assert _bwd(lib, ws=G) == mt.E_ALIAS              # workspace over dXr
 
 
+def _gbwd(lib, **kw):
+    a = dict(X=A, Wg=A + 0x1000, Wu=A + 0x2000, W2r=A + 0x3000, G=A + 0x4000, U=A + 0x5000,
+             H=A + 0x6000, dY=A + 0x7000, dG=B, dU=B + 0x1000, dWg=C, dWu=C + 0x1000, dW2r=E,
+             dXr=G, N=4, D=8, F=16, T=2, dtype=mt.BF16)
+    a.update(kw)
+    return lib.mlp_tp_swiglu_shard_bwd(a["X"], a["Wg"], a["Wu"], a["W2r"], a["G"], a["U"],
+                                       a["H"], a["dY"], a["dG"], a["dU"], a["dWg"], a["dWu"],
+                                       a["dW2r"], a["dXr"], a["N"], a["D"], a["F"], a["T"],
+                                       a["dtype"], S)
+
+
+def test_swiglu_shard_bwd_argument_checks(lib):
+    # Gated backward [Z 08]: every pointer is required, and no output may overlap anything.
+    for k in ("X", "Wg", "Wu", "W2r", "G", "U", "H", "dY", "dG", "dU", "dWg", "dWu", "dW2r",
+              "dXr"):
+        assert _gbwd(lib, **{k: None}) == mt.E_NULL, k
+    assert _gbwd(lib, T=3) == mt.E_INDIVISIBLE
+    assert _gbwd(lib, T=0) == mt.E_SHAPE
+    assert _gbwd(lib, N=-1) == mt.E_SHAPE
+    assert _gbwd(lib, dtype=9) == mt.E_DTYPE
+    assert _gbwd(lib, dU=B + 0x1008) == mt.E_ALIGN
+    assert _gbwd(lib, dG=A + 0x4000) == mt.E_ALIAS    # dG over G
+    assert _gbwd(lib, dU=B + 0x10) == mt.E_ALIAS      # dU inside dG
+    assert _gbwd(lib, dXr=A + 0x7000) == mt.E_ALIAS   # dX partial over dY
+    assert _gbwd(lib, dWu=C) == mt.E_ALIAS            # two weight gradients on one buffer
+
+
 def test_header_has_no_torch_or_hip_types():
     with open(mt.HEADER) as f:
         text = f.read()

@@ -177,6 +177,93 @@ def test_llama70b_gated_shard_full_size():
     assert_close("P rows", s.P[rows], P)
 
 
+def _run_gated_bwd(w, X, s, dY):
+    dev = "cuda"
+    out = {
+        "dG": torch.empty((w.N, w.Fs), dtype=_tdt(w), device=dev),
+        "dU": torch.empty((w.N, w.Fs), dtype=_tdt(w), device=dev),
+        "dWg": torch.empty((w.D, w.Fs), dtype=torch.float32, device=dev),
+        "dWu": torch.empty((w.D, w.Fs), dtype=torch.float32, device=dev),
+        "dW2": torch.empty((w.Fs, w.D), dtype=torch.float32, device=dev),
+        "dX": torch.empty((w.N, w.D), dtype=torch.float32, device=dev),
+    }
+    mt.mlp_tp_swiglu_shard_bwd(X, s.dWg, s.dWu, s.dW2, s.G, s.U, s.H, dY, out["dG"], out["dU"],
+                               out["dWg"], out["dWu"], out["dW2"], out["dX"], w.N, w.D, w.F,
+                               w.T, _dt(w))
+    return out
+
+
+GATED_GRADS = ("dG", "dU", "dWg", "dWu", "dW2", "dX")
+
+
+@pytest.mark.parametrize("w", GATED, ids=lambda w: w.name)
+def test_gated_backward_shards_and_summed_dx(w):
+    """Every rank's gated gradients against the oracle (product rule through SiLU(G) * U
+    [Z 08]); the dX partials summed over the ranks against the unsharded gated MLP's dX."""
+    _say(f"  workload {w.name}")
+    Xc, dYc = synth.gen_X(w), synth.gen_dY(w)
+    X, dY = Xc.cuda(), dYc.cuda()
+    tol = 1e-5 if w.dtype == "f32" else TOL
+    parts = []
+    for r in range(w.T):
+        s = GatedShard(w, X, r)
+        g = _run_gated_bwd(w, X, s, dY)
+        torch.cuda.synchronize()
+        ref = oracle.swiglu_shard_bwd(Xc, s.Wg, s.Wu, s.W2, dYc, 1, 0)
+        for k in GATED_GRADS:
+            assert_close(f"{k}[{r}]", g[k], ref[k], tol)
+        parts.append(g["dX"])
+    dX = torch.empty((w.N, w.D), device="cuda")
+    mt.mlp_tp_partial_reduce(parts, w.T, None, mt.F32, dX, w.N, w.D)
+    torch.cuda.synchronize()
+    dense = oracle.swiglu_shard_bwd(Xc, synth.gen_Wg(w), synth.gen_Wu(w), synth.gen_W2(w), dYc,
+                                    1, 0)
+    assert_close("sum dX", dX, dense["dX"], tol)
+
+
+def test_gated_backward_zero_tokens_zeroes_weight_gradients():
+    """N = 0: dG, dU and dX are empty; the weight gradients are empty sums, written as 0."""
+    D, F, T = 64, 128, 2
+    Fs = F // T
+    Wg = torch.randn((D, Fs), device="cuda").bfloat16()
+    Wu = torch.randn((D, Fs), device="cuda").bfloat16()
+    W2 = torch.randn((Fs, D), device="cuda").bfloat16()
+    d = [torch.full((16,), 3.0, device="cuda") for _ in range(8)]
+    dWg = torch.full((D, Fs), 5.0, device="cuda")
+    dWu = torch.full((D, Fs), 5.0, device="cuda")
+    dW2 = torch.full((Fs, D), 5.0, device="cuda")
+    mt.mlp_tp_swiglu_shard_bwd(d[0], Wg, Wu, W2, d[1], d[2], d[3], d[4], d[5], d[6], dWg, dWu,
+                               dW2, d[7], 0, D, F, T, mt.BF16)
+    torch.cuda.synchronize()
+    for t in (dWg, dWu, dW2):
+        assert torch.all(t == 0.0)
+    for t in d:
+        assert torch.all(t == 3.0)
+
+
+def test_llama70b_gated_backward_full_size():
+    """Gated backward of the Llama-3-70B FFN shard (N=4096, D=8192, F/T=3584), dY ~ N(0,1):
+    dG, dU and dX^(0) on sampled token rows; dWg, dWu and dW2 on sampled hidden columns."""
+    w = workloads.LLAMA70B_SWIGLU_SHARD_T8
+    _say(f"  workload {w.name}")
+    Xc, dYc = synth.gen_X(w), synth.gen_dY(w)
+    X, dY = Xc.cuda(), dYc.cuda()
+    s = GatedShard(w, X, 0)
+    g = _run_gated_bwd(w, X, s, dY)
+    torch.cuda.synchronize()
+    rows = _sample(w.N, 4, 14)
+    cols = _sample(w.Fs, 4, 15)
+    ref_rows = oracle.swiglu_shard_bwd(Xc[rows], s.Wg, s.Wu, s.W2, dYc[rows], 1, 0)
+    for k in ("dG", "dU", "dX"):
+        assert_close(f"{k} rows", g[k][rows], ref_rows[k])
+    ref_cols = oracle.swiglu_shard_bwd(Xc, s.Wg[:, cols], s.Wu[:, cols], s.W2[cols, :], dYc, 1,
+                                       0)
+    assert_close("dG cols", g["dG"][:, cols], ref_cols["dG"])
+    for k in ("dWg", "dWu"):
+        assert_close(f"{k} cols", g[k][:, cols], ref_cols[k])
+    assert_close("dW2 cols", g["dW2"][cols, :], ref_cols["dW2"])
+
+
 # --------------------------------------------------------------------------------------------
 # Block tail, reduce-scatter layout [Z 04]
 # --------------------------------------------------------------------------------------------
