@@ -33,6 +33,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "TP-shard MLP fwd TFLOP/s + % bf16 MFMA peak (D=8192, F/T=3584, N=4096)"
+WARMUP_MS = 250.0      # headline: from idle the clocks settle after ~40 ms of load
+ROW_WARMUP_MS = 150.0  # each extra row, after its own input set-up
+
 ROWS = ("fwd_cold_operands", "partial_reduce", "shard_bwd", "sum_dx", "gated_shard_fwd",
         "gated_shard_bwd", "gpt3_layer", "reduce_scatter_slice", "shard_count_sweep")
 
@@ -71,6 +74,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-ms", type=float, default=WARMUP_MS,
+                    help="untimed warmup runs at least --warmup steps and at least this much "
+                         "GPU time: from idle the GPU's clocks take ~40 ms of load to settle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the extra per-row timings")
     ap.add_argument("--rows", default="all",
@@ -121,10 +127,8 @@ def main() -> int:
         mt.mlp_tp_up_proj(X, W1, b1, None, H, N, D, F, T, mt.BF16, w.act)
         mt.mlp_tp_down_proj(H, W2, P, N, D, F, T, mt.BF16)
 
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_steps, warm_ms = warm_up(torch, step, args.warmup, args.warmup_ms)
+    log(f"[bench] warmup {warm_steps} steps, {warm_ms:.0f} ms")
 
     # Timed region: K steps, HIP events between the two launches of every step (all on
     # torch's current stream, which is the stream the binding launches on).
@@ -193,7 +197,8 @@ def main() -> int:
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warm_steps,
+        "warmup_ms": round(warm_ms, 1),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -212,10 +217,34 @@ def main() -> int:
     return 0
 
 
-def _time_loop(torch, fn, iters, warm=3):
-    for _ in range(warm):
-        fn()
+def warm_up(torch, fn, min_calls, min_ms, chunk=8):
+    """Runs fn at least `min_calls` times and for at least `min_ms` of GPU time, untimed.
+
+    From idle, the GPU's clocks ramp up over the first ~40 ms of sustained load (a 50 ms pause
+    is enough to drop them again), so a fixed handful of warmup calls leaves the timed region
+    inside the ramp. Calls are issued in chunks with at most two chunks in flight, so the GPU
+    never idles while the host checks the elapsed time. Returns (calls, GPU ms)."""
+    s = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t0.record(s)
+    calls, pending = 0, None
+    while True:
+        for _ in range(chunk):
+            fn()
+        calls += chunk
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(s)
+        if pending is not None:
+            pending.synchronize()
+            if calls - chunk >= min_calls and t0.elapsed_time(pending) >= min_ms:
+                break
+        pending = ev
     torch.cuda.synchronize()
+    return calls, t0.elapsed_time(ev)
+
+
+def _time_loop(torch, fn, iters, warm_ms=None):
+    warm_up(torch, fn, 3, ROW_WARMUP_MS if warm_ms is None else warm_ms)
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     s = torch.cuda.current_stream()
@@ -253,11 +282,15 @@ def _row_cold(torch, mt, dev, X, W1, b1, W2, H, w, copies=3):
     steps = 10 * copies
     s = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(2 * copies):
-        Xi, W1i, b1i, W2i = sets[i % copies]
+    turn = [0]
+
+    def rotating_step():
+        Xi, W1i, b1i, W2i = sets[turn[0] % copies]
+        turn[0] += 1
         mt.mlp_tp_up_proj(Xi, W1i, b1i, None, H, N, D, F, T, mt.BF16, w.act)
         mt.mlp_tp_down_proj(H, W2i, P, N, D, F, T, mt.BF16)
-    torch.cuda.synchronize()
+
+    warm_up(torch, rotating_step, 2 * copies, ROW_WARMUP_MS)
     for i in range(steps):
         Xi, W1i, b1i, W2i = sets[i % copies]
         ev[i][0].record(s)

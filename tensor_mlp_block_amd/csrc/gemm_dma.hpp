@@ -17,7 +17,8 @@
 //     group the transpose read returns lane i the i-th element of the four 16-element rows the
 //     group's lanes address, i.e. 4 consecutive k of one output row.
 //   * Two LDS stages: loads of stage k+1 are issued before the MFMAs of stage k; a vmcnt wait
-//     and one barrier end each stage.
+//     and one barrier end each stage. Within a stage the LDS reads are interleaved with the
+//     MFMAs, two B fragments ahead of their use (dma_step).
 #pragma once
 
 #include "lds_dma.hpp"
@@ -172,10 +173,34 @@ __device__ __forceinline__ void dma_issue(const DmaCtx& c, int64_t kt, MLPTP_LDS
     }
 }
 
+// sched_group_barrier over n LDS reads, for an n that is a constant only after unrolling: one
+// call with a literal per case; the switch folds to the case taken.
+__device__ __forceinline__ void sched_ds_reads(int n)
+{
+    switch (n) {
+#define MLPTP_SGB(k) case k: __builtin_amdgcn_sched_group_barrier(0x100, k, 0); break;
+        MLPTP_SGB(1) MLPTP_SGB(2) MLPTP_SGB(3) MLPTP_SGB(4) MLPTP_SGB(5) MLPTP_SGB(6)
+        MLPTP_SGB(7) MLPTP_SGB(8) MLPTP_SGB(9) MLPTP_SGB(10) MLPTP_SGB(11) MLPTP_SGB(12)
+        MLPTP_SGB(13) MLPTP_SGB(14) MLPTP_SGB(15) MLPTP_SGB(16) MLPTP_SGB(17) MLPTP_SGB(18)
+        MLPTP_SGB(19) MLPTP_SGB(20) MLPTP_SGB(21) MLPTP_SGB(22) MLPTP_SGB(23) MLPTP_SGB(24)
+#undef MLPTP_SGB
+    default: break;
+    }
+}
+
 // One pipeline step: start the loads of stage `next_kt` (if >= 0) into `nxt`, then run the
 // MFMAs of the stage held in `cur`. `cur` and `nxt` are distinct stages; the __restrict__
 // qualifiers tell the compiler so, which lets it read `cur` while the loads into `nxt` are
 // still in flight instead of waiting for them first.
+//
+// Instruction order. The MFMAs go B fragment by B fragment (each B fragment meets the wave's
+// FM A fragments), and the LDS reads are interleaved with them two fragments ahead: the A
+// fragments of a k-substep and its first two B fragments are read before its first MFMA, and
+// after each group of FM MFMAs the B fragment two places ahead is read (at a substep boundary,
+// with the next substep's A fragments first). Left to itself the compiler issued all of a
+// stage's reads before its first MFMA; the hardware tracks at most 15 outstanding LDS reads
+// per wave, so the first MFMA then waited for half of them, on both waves of every SIMD at
+// once (they leave the stage barrier together).
 template <class Cfg, bool A_KC, bool B_KC, bool DUAL>
 __device__ __attribute__((always_inline)) inline void dma_step(
     const DmaCtx& c, int64_t next_kt, const MLPTP_LDS uint8_t* __restrict__ cur,
@@ -208,10 +233,26 @@ __device__ __attribute__((always_inline)) inline void dma_step(
             }
         }
 #pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i)
+        for (int j = 0; j < Cfg::FN; ++j)
 #pragma unroll
-            for (int j = 0; j < Cfg::FN; ++j)
+            for (int i = 0; i < Cfg::FM; ++i)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    }
+    // The interleave: LDS instructions per fragment are 1 (k-contiguous tile, one b128 read) or
+    // 2 (transpose reads); fragment f of the stage's FN * KSUB B fragments is preceded by its
+    // substep's A fragments when it is the substep's first.
+    constexpr int AR = A_KC ? 1 : 2, BR = B_KC ? 1 : 2, L = 2;
+    constexpr int G = Cfg::KSUB * Cfg::FN;
+    auto reads_of = [](int f) { return ((f % Cfg::FN) == 0 ? Cfg::FM * AR : 0) + BR; };
+    static_assert(Cfg::FM * AR + L * BR <= 24, "first read group larger than sched_ds_reads takes");
+    int first = 0;
+#pragma unroll
+    for (int f = 0; f < L && f < G; ++f) first += reads_of(f);
+    sched_ds_reads(first);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, Cfg::FM, 0);  // FM MFMAs
+        if (g + L < G) sched_ds_reads(reads_of(g + L));
     }
 }
 
