@@ -256,6 +256,24 @@ __device__ __attribute__((always_inline)) inline void dma_step(
     }
 }
 
+// For a pair of accumulator fragments a (columns c..c+15) and b (columns c+16..c+31) of the
+// same 16 rows, where lane 16 g + r holds row r, columns 4 g..4 g+3 of each: x gets a on lanes
+// r < 8 and, on lanes r >= 8, b of lane r - 8 (row r - 8); y gets a on lanes r >= 8 and, on
+// lanes r < 8, b of lane r + 8 (row r + 8). Two DPP row shifts by 8 with bank masks (a bank is 4
+// lanes of a 16-lane row; the masked-off lanes keep a).
+__device__ __forceinline__ void swap_row_halves(const f32x4& a, const f32x4& b, f32x4& x, f32x4& y)
+{
+    // Each element is copied to a scalar before its bit pattern is taken: a bit cast of a vector
+    // element expression reads the vector's first element, whichever element is named.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float ae = a[e], be = b[e];
+        const int ai = __float_as_int(ae), bi = __float_as_int(be);
+        x[e] = __int_as_float(__builtin_amdgcn_update_dpp(ai, bi, 0x118, 0xF, 0xC, false));
+        y[e] = __int_as_float(__builtin_amdgcn_update_dpp(ai, bi, 0x108, 0xF, 0x3, false));
+    }
+}
+
 // Whether an epilogue takes the dual form (two results per output element, from B and B2).
 template <class E, class = void>
 struct EpiIsDual : std::false_type {};
@@ -331,8 +349,30 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void gemm_bf16_dma(
                 epi.apply_dual(row, col, acc[i][j], acc[i][j + Cfg::FN / 2], M, N);
             }
         } else {
+            // Fragments j and j+1 are 32 adjacent columns of the same 16 rows. Handed out as
+            // they are, each store instruction would write 16 rows x 16 columns: half of each
+            // row's 128-byte line in fp32, and a streaming store then reaches HBM as separate
+            // partial-line writes. Instead lanes 8-15 of every 16-lane row swap their fragment
+            // j+1 values with lanes 0-7's fragment j+1 values: the first store covers rows
+            // 0-7 and the second rows 8-15, each row's 32 columns whole.
+            const bool hi = frow >= 8;
+            const int64_t row_lo = m0 + wm * Cfg::WTM + i * 16 + (frow & 7);
 #pragma unroll
-            for (int j = 0; j < Cfg::FN; ++j) {
+            for (int j = 0; j + 1 < Cfg::FN; j += 2) {
+                const int64_t c0 = n0 + wn * Cfg::WTN + j * 16 + 4 * fchunk;
+                f32x4 x, y;
+                swap_row_halves(acc[i][j], acc[i][j + 1], x, y);
+                const int64_t cx = c0 + (hi ? 16 : 0), cy = c0 + (hi ? 0 : 16);
+                if constexpr (Epi::kColData) {
+                    epi.apply(row_lo, cx, x, hi ? cdat[j + 1] : cdat[j], {}, M, N);
+                    epi.apply(row_lo + 8, cy, y, hi ? cdat[j] : cdat[j + 1], {}, M, N);
+                } else {
+                    epi(row_lo, cx, x, M, N);
+                    epi(row_lo + 8, cy, y, M, N);
+                }
+            }
+            if constexpr (Cfg::FN % 2 != 0) {
+                constexpr int j = Cfg::FN - 1;
                 const int64_t col = n0 + wn * Cfg::WTN + j * 16 + 4 * fchunk;
                 if constexpr (Epi::kColData)
                     epi.apply(row, col, acc[i][j], cdat[j], {}, M, N);
