@@ -343,10 +343,24 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void gemm_bf16_dma(
     for (int i = 0; i < Cfg::FM; ++i) {
         const int64_t row = m0 + wm * Cfg::WTM + i * 16 + frow;
         if constexpr (DUAL) {
+            // As below for the single form, per half: fragments j and j+1 of each half are 32
+            // adjacent output columns.
+            constexpr int HF = Cfg::FN / 2;
+            const bool hi = frow >= 8;
+            const int64_t row_lo = m0 + wm * Cfg::WTM + i * 16 + (frow & 7);
 #pragma unroll
-            for (int j = 0; j < Cfg::FN / 2; ++j) {
+            for (int j = 0; j + 1 < HF; j += 2) {
+                const int64_t c0 = n0 + wn * WTNO + j * 16 + 4 * fchunk;
+                f32x4 gx, gy, ux, uy;
+                swap_row_halves(acc[i][j], acc[i][j + 1], gx, gy);
+                swap_row_halves(acc[i][HF + j], acc[i][HF + j + 1], ux, uy);
+                epi.apply_dual(row_lo, c0 + (hi ? 16 : 0), gx, ux, M, N);
+                epi.apply_dual(row_lo + 8, c0 + (hi ? 0 : 16), gy, uy, M, N);
+            }
+            if constexpr (HF % 2 != 0) {
+                constexpr int j = HF - 1;
                 const int64_t col = n0 + wn * WTNO + j * 16 + 4 * fchunk;
-                epi.apply_dual(row, col, acc[i][j], acc[i][j + Cfg::FN / 2], M, N);
+                epi.apply_dual(row, col, acc[i][j], acc[i][j + HF], M, N);
             }
         } else {
             // Fragments j and j+1 are 32 adjacent columns of the same 16 rows. Handed out as
