@@ -16,9 +16,9 @@
 //     k-contiguous tile, or with two ds_read_b64_tr_b16 from a [k][rows] tile: in each 16-lane
 //     group the transpose read returns lane i the i-th element of the four 16-element rows the
 //     group's lanes address, i.e. 4 consecutive k of one output row.
-//   * Two LDS stages: loads of stage k+1 are issued before the MFMAs of stage k; a vmcnt wait
-//     and one barrier end each stage. Within a stage the LDS reads are interleaved with the
-//     MFMAs, two B fragments ahead of their use (dma_step).
+//   * Two LDS stages: the loads of stage k+1 are issued while the MFMAs of stage k run; a vmcnt
+//     wait and one barrier end each stage. Within a stage the loads and the LDS reads are
+//     interleaved with the MFMAs, the reads two B fragments ahead of their use (dma_step).
 #pragma once
 
 #include "lds_dma.hpp"
@@ -71,7 +71,7 @@ __device__ __forceinline__ int mc_swz(int k)
         return (k & 3) << 1;
 }
 
-// Issues this wave's share of the global->LDS copy of one operand tile (ROWS x 64 k).
+// Issues load q of this wave's share of the global->LDS copy of one operand tile (ROWS x 64 k).
 //   KC: element (row, k) at src[row * ld + k]; LDS [ROWS][64].
 //   MC: element (row, k) at src[k * ld + row]; LDS [64][ROWS].
 // `src` already points at (row0, k0); rows >= rows_left or k >= k_left load zeros. One buffer
@@ -80,37 +80,42 @@ __device__ __forceinline__ int mc_swz(int k)
 // swizzled chunk. (Out-of-range lanes carry an offset of 2^31 in the vector operand, past the
 // resource's range whether or not the hardware adds the scalar offset before its check.)
 template <int ROWS, int NWAVES, bool KC>
-__device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t ld, int rows_left,
-                                         int k_left, MLPTP_LDS uint8_t* lds, int wave, int lane)
+__device__ __forceinline__ void dma_load_one(const uint16_t* src, int64_t ld, int rows_left,
+                                             int k_left, MLPTP_LDS uint8_t* lds, int wave, int lane,
+                                             int q)
 {
     constexpr int kInstr = ROWS * 64 * 2 / 1024;  // 1 KB wave loads per tile
+    const int qi = q * NWAVES + wave;
+    if (kInstr % NWAVES != 0 && qi >= kInstr) return;  // wave-uniform
     const i32x4 rsrc = make_buffer_rsrc(src);
-#pragma unroll
-    for (int q = 0; q < (kInstr + NWAVES - 1) / NWAVES; ++q) {
-        const int qi = q * NWAVES + wave;
-        if (kInstr % NWAVES != 0 && qi >= kInstr) break;  // wave-uniform
-        int off;
-        int first;  // first row (KC) or k row (MC) of this load
-        if (KC) {
-            first = qi * 8;
-            const int rl = lane >> 3;
-            const int c = (lane & 7) ^ kc_swz(first + rl);
-            const bool ok = rl < rows_left - first && c * 8 < k_left;
-            off = ok ? (int)(rl * ld * 2 + c * 16) : kOutOfRange;
-        } else {
-            // Chunk index idx = 64 qi + lane lands at byte 16 idx = k * 2 ROWS + 16 p.
-            constexpr int kChunks = ROWS / 8;
-            first = (qi * 64) / kChunks;
-            const int idx = qi * 64 + lane;
-            const int k = idx / kChunks;
-            const int c = (idx % kChunks) ^ mc_swz<ROWS>(k);
-            const bool ok = k < k_left && c * 8 < rows_left;
-            off = ok ? (int)((k - first) * ld * 2 + c * 16) : kOutOfRange;
-        }
-        const int soff = __builtin_amdgcn_readfirstlane((int)(first * ld * 2));
-        llvm_amdgcn_raw_buffer_load_lds(rsrc, reinterpret_cast<MLPTP_LDS uint32_t*>(lds + qi * 1024),
-                                        16, off, soff, 0, 0);
+    int off;
+    int first;  // first row (KC) or k row (MC) of this load
+    if (KC) {
+        first = qi * 8;
+        const int rl = lane >> 3;
+        const int c = (lane & 7) ^ kc_swz(first + rl);
+        const bool ok = rl < rows_left - first && c * 8 < k_left;
+        off = ok ? (int)(rl * ld * 2 + c * 16) : kOutOfRange;
+    } else {
+        // Chunk index idx = 64 qi + lane lands at byte 16 idx = k * 2 ROWS + 16 p.
+        constexpr int kChunks = ROWS / 8;
+        first = (qi * 64) / kChunks;
+        const int idx = qi * 64 + lane;
+        const int k = idx / kChunks;
+        const int c = (idx % kChunks) ^ mc_swz<ROWS>(k);
+        const bool ok = k < k_left && c * 8 < rows_left;
+        off = ok ? (int)((k - first) * ld * 2 + c * 16) : kOutOfRange;
     }
+    const int soff = __builtin_amdgcn_readfirstlane((int)(first * ld * 2));
+    llvm_amdgcn_raw_buffer_load_lds(rsrc, reinterpret_cast<MLPTP_LDS uint32_t*>(lds + qi * 1024), 16,
+                                    off, soff, 0, 0);
+}
+
+// Loads per wave for one operand tile of ROWS x 64 k.
+template <int ROWS, int NWAVES>
+constexpr int dma_loads_per_wave()
+{
+    return (ROWS * 64 * 2 / 1024 + NWAVES - 1) / NWAVES;
 }
 
 // One MFMA operand fragment (16 rows x 32 k) for k-step ks from a KC tile.
@@ -150,110 +155,153 @@ struct DmaCtx {
     int m_left, n_left, wave, lane;
 };
 
-// Loads of stage kt. In the dual form the B tile is two tiles of BN/2 columns, the same output
-// columns of B and of B2, side by side in LDS.
+// Global sources of stage kt's tiles. In the dual form the B tile is two tiles of BN/2 columns,
+// the same output columns of B and of B2, side by side in LDS. A kt past the last stage gives an
+// empty k range: every lane of its loads takes the out-of-range offset and loads zeros.
+struct StageSrc {
+    const uint16_t* a;
+    const uint16_t* b;
+    const uint16_t* b2;
+    int k_left;
+};
+
+template <class Cfg, bool A_KC, bool B_KC, bool DUAL>
+__device__ __forceinline__ StageSrc stage_src(const DmaCtx& c, int64_t kt)
+{
+    const int64_t k0 = kt * Cfg::BK;
+    StageSrc t;
+    t.k_left = (int)((c.K - k0) < Cfg::BK ? (c.K - k0) : Cfg::BK);
+    t.a = A_KC ? c.A + c.m0 * c.lda + k0 : c.A + k0 * c.lda + c.m0;
+    t.b = B_KC ? c.B + c.n0 * c.ldb + k0 : c.B + k0 * c.ldb + c.n0;
+    t.b2 = DUAL ? (B_KC ? c.B2 + c.n0 * c.ldb + k0 : c.B2 + k0 * c.ldb + c.n0) : nullptr;
+    return t;
+}
+
+// Loads per wave for a whole stage: the A tile's, then the B tile's (both halves in the dual form).
+template <class Cfg, bool DUAL>
+struct StageLoads {
+    static constexpr int QA = dma_loads_per_wave<Cfg::BM, Cfg::NWAVES>();
+    static constexpr int QH = dma_loads_per_wave<Cfg::BN / 2, Cfg::NWAVES>();
+    static constexpr int QB = DUAL ? 2 * QH : dma_loads_per_wave<Cfg::BN, Cfg::NWAVES>();
+    static constexpr int Q = QA + QB;
+};
+
+// Load q (0 <= q < StageLoads::Q) of this wave's share of a stage.
+template <class Cfg, bool A_KC, bool B_KC, bool DUAL>
+__device__ __forceinline__ void stage_load(const DmaCtx& c, const StageSrc& t,
+                                           MLPTP_LDS uint8_t* base, int q)
+{
+    using SL = StageLoads<Cfg, DUAL>;
+    if (q < SL::QA) {
+        dma_load_one<Cfg::BM, Cfg::NWAVES, A_KC>(t.a, c.lda, c.m_left, t.k_left, base, c.wave,
+                                                 c.lane, q);
+    } else if constexpr (!DUAL) {
+        dma_load_one<Cfg::BN, Cfg::NWAVES, B_KC>(t.b, c.ldb, c.n_left, t.k_left,
+                                                 base + Cfg::A_BYTES, c.wave, c.lane, q - SL::QA);
+    } else {
+        constexpr int HB = Cfg::BN / 2;
+        if (q < SL::QA + SL::QH)
+            dma_load_one<HB, Cfg::NWAVES, B_KC>(t.b, c.ldb, c.n_left, t.k_left,
+                                                base + Cfg::A_BYTES, c.wave, c.lane, q - SL::QA);
+        else
+            dma_load_one<HB, Cfg::NWAVES, B_KC>(t.b2, c.ldb, c.n_left, t.k_left,
+                                                base + Cfg::A_BYTES + Cfg::B_BYTES / 2, c.wave,
+                                                c.lane, q - SL::QA - SL::QH);
+    }
+}
+
+// All loads of stage kt (the pipeline's first stage).
 template <class Cfg, bool A_KC, bool B_KC, bool DUAL>
 __device__ __forceinline__ void dma_issue(const DmaCtx& c, int64_t kt, MLPTP_LDS uint8_t* base)
 {
-    const int64_t k0 = kt * Cfg::BK;
-    const int k_left = (int)((c.K - k0) < Cfg::BK ? (c.K - k0) : Cfg::BK);
-    const uint16_t* a = A_KC ? c.A + c.m0 * c.lda + k0 : c.A + k0 * c.lda + c.m0;
-    const uint16_t* b = B_KC ? c.B + c.n0 * c.ldb + k0 : c.B + k0 * c.ldb + c.n0;
-    dma_tile<Cfg::BM, Cfg::NWAVES, A_KC>(a, c.lda, c.m_left, k_left, base, c.wave, c.lane);
-    if constexpr (!DUAL) {
-        dma_tile<Cfg::BN, Cfg::NWAVES, B_KC>(b, c.ldb, c.n_left, k_left, base + Cfg::A_BYTES,
-                                             c.wave, c.lane);
-    } else {
-        constexpr int HB = Cfg::BN / 2;
-        const uint16_t* b2 = B_KC ? c.B2 + c.n0 * c.ldb + k0 : c.B2 + k0 * c.ldb + c.n0;
-        dma_tile<HB, Cfg::NWAVES, B_KC>(b, c.ldb, c.n_left, k_left, base + Cfg::A_BYTES, c.wave,
-                                        c.lane);
-        dma_tile<HB, Cfg::NWAVES, B_KC>(b2, c.ldb, c.n_left, k_left,
-                                        base + Cfg::A_BYTES + Cfg::B_BYTES / 2, c.wave, c.lane);
-    }
+    const StageSrc t = stage_src<Cfg, A_KC, B_KC, DUAL>(c, kt);
+#pragma unroll
+    for (int q = 0; q < StageLoads<Cfg, DUAL>::Q; ++q) stage_load<Cfg, A_KC, B_KC, DUAL>(c, t, base, q);
 }
 
-// sched_group_barrier over n LDS reads, for an n that is a constant only after unrolling: one
-// call with a literal per case; the switch folds to the case taken.
-__device__ __forceinline__ void sched_ds_reads(int n)
-{
-    switch (n) {
-#define MLPTP_SGB(k) case k: __builtin_amdgcn_sched_group_barrier(0x100, k, 0); break;
-        MLPTP_SGB(1) MLPTP_SGB(2) MLPTP_SGB(3) MLPTP_SGB(4) MLPTP_SGB(5) MLPTP_SGB(6)
-        MLPTP_SGB(7) MLPTP_SGB(8) MLPTP_SGB(9) MLPTP_SGB(10) MLPTP_SGB(11) MLPTP_SGB(12)
-        MLPTP_SGB(13) MLPTP_SGB(14) MLPTP_SGB(15) MLPTP_SGB(16) MLPTP_SGB(17) MLPTP_SGB(18)
-        MLPTP_SGB(19) MLPTP_SGB(20) MLPTP_SGB(21) MLPTP_SGB(22) MLPTP_SGB(23) MLPTP_SGB(24)
-#undef MLPTP_SGB
-    default: break;
-    }
-}
-
-// One pipeline step: start the loads of stage `next_kt` (if >= 0) into `nxt`, then run the
-// MFMAs of the stage held in `cur`. `cur` and `nxt` are distinct stages; the __restrict__
-// qualifiers tell the compiler so, which lets it read `cur` while the loads into `nxt` are
-// still in flight instead of waiting for them first.
+// One pipeline step: the MFMAs of the stage held in `cur`, and the loads of stage `next_kt` into
+// `nxt` (past the last stage: loads of an empty k range). `cur` and `nxt` are distinct stages; the
+// __restrict__ qualifiers tell the compiler so, which lets it read `cur` while the loads into
+// `nxt` are still in flight instead of waiting for them first.
 //
-// Instruction order. The MFMAs go B fragment by B fragment (each B fragment meets the wave's
-// FM A fragments), and the LDS reads are interleaved with them two fragments ahead: the A
-// fragments of a k-substep and its first two B fragments are read before its first MFMA, and
-// after each group of FM MFMAs the B fragment two places ahead is read (at a substep boundary,
-// with the next substep's A fragments first). Left to itself the compiler issued all of a
-// stage's reads before its first MFMA; the hardware tracks at most 15 outstanding LDS reads
-// per wave, so the first MFMA then waited for half of them, on both waves of every SIMD at
-// once (they leave the stage barrier together).
+// The order is written out, because the compiler keeps LDS reads after an LDS-writing load that
+// precedes them in the source: the MFMAs go B fragment by B fragment (each meets the wave's FM A
+// fragments); after each group of FM MFMAs come one of the wave's loads of the next stage and the
+// reads of the B fragment two places ahead (at a k-substep boundary, with that substep's A
+// fragments first). Left to itself the compiler put every load and all 30-40 reads of a stage
+// ahead of its first MFMA: a wave tracks at most 15 outstanding LDS reads, so that MFMA waited for
+// about half of them, and both waves of every SIMD did this at the same moment after the barrier.
 template <class Cfg, bool A_KC, bool B_KC, bool DUAL>
 __device__ __attribute__((always_inline)) inline void dma_step(
     const DmaCtx& c, int64_t next_kt, const MLPTP_LDS uint8_t* __restrict__ cur,
     MLPTP_LDS uint8_t* __restrict__ nxt, f32x4 (&acc)[Cfg::FM][Cfg::FN], int wm, int wn)
 {
-    if (next_kt >= 0) dma_issue<Cfg, A_KC, B_KC, DUAL>(c, next_kt, nxt);
+    using SL = StageLoads<Cfg, DUAL>;
+    const StageSrc src =
+        stage_src<Cfg, A_KC, B_KC, DUAL>(c, next_kt >= 0 ? next_kt : ceil_div(c.K, (int64_t)Cfg::BK));
     const MLPTP_LDS uint8_t* As = cur;
     const MLPTP_LDS uint8_t* Bs = cur + Cfg::A_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < Cfg::KSUB; ++ks) {
-        bf16x8 af[Cfg::FM], bfr[Cfg::FN];
+    constexpr int G = Cfg::KSUB * Cfg::FN, L = 2;
+    bf16x8 af[Cfg::KSUB][Cfg::FM], bfr[G];
+    auto read_a = [&](int ks) {
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
             const int row = wm * Cfg::WTM + i * 16;
-            af[i] = A_KC ? frag_kc<Cfg::BM>(As, row, ks, c.lane) : frag_mc<Cfg::BM>(As, row, ks, c.lane);
+            af[ks][i] = A_KC ? frag_kc<Cfg::BM>(As, row, ks, c.lane)
+                             : frag_mc<Cfg::BM>(As, row, ks, c.lane);
         }
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) {
-            if constexpr (!DUAL) {
-                const int row = wn * Cfg::WTN + j * 16;
-                bfr[j] = B_KC ? frag_kc<Cfg::BN>(Bs, row, ks, c.lane)
-                              : frag_mc<Cfg::BN>(Bs, row, ks, c.lane);
-            } else {
-                // Fragments 0 .. FN/2-1 from the first B tile, the rest from the second, at the
-                // same columns: acc[i][j] and acc[i][j + FN/2] hold the same outputs of B and B2.
-                constexpr int HB = Cfg::BN / 2, HF = Cfg::FN / 2;
-                const MLPTP_LDS uint8_t* Bh = Bs + (j / HF) * (Cfg::B_BYTES / 2);
-                const int row = wn * (Cfg::WTN / 2) + (j % HF) * 16;
-                bfr[j] = B_KC ? frag_kc<HB>(Bh, row, ks, c.lane) : frag_mc<HB>(Bh, row, ks, c.lane);
-            }
+    };
+    auto read_b = [&](int f) {
+        const int ks = f / Cfg::FN, j = f % Cfg::FN;
+        if constexpr (!DUAL) {
+            const int row = wn * Cfg::WTN + j * 16;
+            bfr[f] = B_KC ? frag_kc<Cfg::BN>(Bs, row, ks, c.lane)
+                          : frag_mc<Cfg::BN>(Bs, row, ks, c.lane);
+        } else {
+            // Fragments 0 .. FN/2-1 from the first B tile, the rest from the second, at the same
+            // columns: acc[i][j] and acc[i][j + FN/2] hold the same outputs of B and B2.
+            constexpr int HB = Cfg::BN / 2, HF = Cfg::FN / 2;
+            const MLPTP_LDS uint8_t* Bh = Bs + (j / HF) * (Cfg::B_BYTES / 2);
+            const int row = wn * (Cfg::WTN / 2) + (j % HF) * 16;
+            bfr[f] = B_KC ? frag_kc<HB>(Bh, row, ks, c.lane) : frag_mc<HB>(Bh, row, ks, c.lane);
         }
+    };
+    // Placement of the next stage's loads: kPerGroup after each MFMA group, from the first. With
+    // a transposed A (the weight-gradient products, whose strided operand loads take longer) two
+    // per group, so they are all in flight within the first half of the stage. Measured on the
+    // bench's rows against loads all up front: one per group was +1-2% on the forward, two per
+    // group +2% on the GPT-3-175B layer's 256x192 tiles, and either was within 1% on the rest.
+    constexpr int kUpFront = 0, kPerGroup = A_KC ? 1 : 2;
+    // A scheduling barrier closes each group: without it the compiler, knowing the loads do not
+    // alias the reads, sank all of a 256x192 tile's loads to the end of the stage, in front of the
+    // wait for them (the GPT-3-175B layer ran 20% slower).
+    constexpr bool kPin = true;
 #pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j)
+    for (int q = 0; q < kUpFront && q < SL::Q; ++q) stage_load<Cfg, A_KC, B_KC, DUAL>(c, src, nxt, q);
+    read_a(0);
 #pragma unroll
-            for (int i = 0; i < Cfg::FM; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
-    // The interleave: LDS instructions per fragment are 1 (k-contiguous tile, one b128 read) or
-    // 2 (transpose reads); fragment f of the stage's FN * KSUB B fragments is preceded by its
-    // substep's A fragments when it is the substep's first.
-    constexpr int AR = A_KC ? 1 : 2, BR = B_KC ? 1 : 2, L = 2;
-    constexpr int G = Cfg::KSUB * Cfg::FN;
-    auto reads_of = [](int f) { return ((f % Cfg::FN) == 0 ? Cfg::FM * AR : 0) + BR; };
-    static_assert(Cfg::FM * AR + L * BR <= 24, "first read group larger than sched_ds_reads takes");
-    int first = 0;
-#pragma unroll
-    for (int f = 0; f < L && f < G; ++f) first += reads_of(f);
-    sched_ds_reads(first);
+    for (int f = 0; f < L && f < G; ++f) read_b(f);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, Cfg::FM, 0);  // FM MFMAs
-        if (g + L < G) sched_ds_reads(reads_of(g + L));
+        const int ks = g / Cfg::FN, j = g % Cfg::FN;
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[g], af[ks][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kPerGroup; ++u) {
+            const int q = kUpFront + g * kPerGroup + u;
+            if (q < SL::Q) stage_load<Cfg, A_KC, B_KC, DUAL>(c, src, nxt, q);
+        }
+        const int f = g + L;
+        if (f < G) {
+            if (f % Cfg::FN == 0) read_a(f / Cfg::FN);
+            read_b(f);
+        }
+        if constexpr (kPin) __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int q = kUpFront + G * kPerGroup; q < SL::Q; ++q)
+        stage_load<Cfg, A_KC, B_KC, DUAL>(c, src, nxt, q);
 }
 
 // For a pair of accumulator fragments a (columns c..c+15) and b (columns c+16..c+31) of the
