@@ -278,9 +278,11 @@ __device__ __attribute__((always_inline)) inline void dma_step(
     constexpr bool kPin = true;
 #pragma unroll
     for (int q = 0; q < kUpFront && q < SL::Q; ++q) stage_load<Cfg, A_KC, B_KC, DUAL>(c, src, nxt, q);
+    // B fragment 0 first: the first MFMA needs it and A fragment 0 only (3 reads, not 6).
+    read_b(0);
     read_a(0);
 #pragma unroll
-    for (int f = 0; f < L && f < G; ++f) read_b(f);
+    for (int f = 1; f < L && f < G; ++f) read_b(f);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const int ks = g / Cfg::FN, j = g % Cfg::FN;

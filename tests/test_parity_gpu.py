@@ -234,6 +234,10 @@ RAGGED = [
     Workload("tile224_n300_d448_f896_t2", 300, 448, 896, 2, "gelu_tanh", "bf16", 7008, "normal"),
     # widths that are multiples of 192: the 256x192 tile (both weight layouts in the backward)
     Workload("tile192_n300_d384_f768_t2", 300, 384, 768, 2, "gelu_tanh", "bf16", 7009, "normal"),
+    # contraction shorter than one 64-deep stage (K = 40 up, 48 down): one partial stage
+    Workload("kshort_n130_d40_f96_t2", 130, 40, 96, 2, "gelu_tanh", "bf16", 7010, "normal"),
+    # contraction of exactly one stage (K = 64 both ways)
+    Workload("kone_n64_d64_f128_t2", 64, 64, 128, 2, "gelu_tanh", "bf16", 7011, "normal"),
 ]
 
 
