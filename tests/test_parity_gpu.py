@@ -263,6 +263,24 @@ def test_forward_block_elementwise(w):
     assert_close("Y", Y, Yref, tol)
 
 
+def test_huge_leading_dimension_takes_register_staged_kernel():
+    """D = 4194368: one 256-row tile of X spans more than 2^31 bytes, past what the direct-to-LDS
+    kernel's 32-bit tile offsets cover, so the up-projection runs on the register-staged kernel
+    (the down-projection's W2 tile spans 64 rows and stays on the direct kernel). Z, H and P
+    against the oracle."""
+    w = Workload("hugeld_n8_d4194368_f16_t1", 8, 4194368, 16, 1, "gelu_tanh", "bf16", 7100,
+                 "normal")
+    _say(f"  workload {w.name}")
+    Xc = synth.gen_X(w)
+    X = Xc.cuda()
+    s = Shard(w, X, 0)
+    torch.cuda.synchronize()
+    Z, H, P = _oracle_shard(w, Xc, s)
+    assert_close("Z", s.Z, Z)
+    assert_close("H", s.H, H)
+    assert_close("P", s.P, P)
+
+
 @pytest.mark.parametrize("w", [x for x in RAGGED if x.act != "relu"], ids=lambda w: w.name)
 def test_backward_shard_elementwise(w):
     """ReLU backward on real-valued data is left to the exact integer test: there the sign of
