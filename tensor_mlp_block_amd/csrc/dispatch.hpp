@@ -15,19 +15,28 @@ using DefaultTile = MfmaTile<128, 128, 2, 2>;
 // Main bf16 tiles: 8 waves per workgroup (two per SIMD). 256 x 256 (waves of 64 x 128) by
 // default; 256 x 224 (64 x 112) and 224 x 256 (112 x 64) when an extent is a multiple of 224 and
 // that tile count fills the GPU's compute units better (e.g. F/T = 3584 = 16 x 224: 256 tiles
-// instead of 224 on 256 CUs).
+// instead of 224 on 256 CUs); 256 x 192 likewise for multiples of 192.
 using DmaTile256x256 = DmaTile<256, 256, 4, 2>;
 using DmaTile256x224 = DmaTile<256, 224, 4, 2>;
 using DmaTile224x256 = DmaTile<224, 256, 2, 4>;
 using DmaTile256x192 = DmaTile<256, 192, 4, 2>;
+// For products with too few 256-wide tiles to fill the GPU: 128 x 128, 4 waves of 64 x 64, two
+// workgroups per CU.
+using DmaTile128x128 = DmaTile<128, 128, 2, 2>;
 
 int compute_units();  // of the current device, queried once
 
-// Estimated cost of a tile shape: rounds of workgroups over the CUs times the tile area.
-inline int64_t tile_cost(int64_t M, int64_t N, int bm, int bn)
+// Estimated time of a tile shape: rounds of workgroups over the CU slots, times the tile area
+// over the tile's throughput relative to one 8-wave 256-class tile per CU. Measured (bf16, the
+// Llama-shape and GPT-2-medium-shape projections): a 128 x 128 workgroup runs at about 0.42 of a
+// 256-class one when two share a CU, so the small tile wins when it fills the GPU in one round
+// and the large tiles do not (a GPT-2-medium shard's down-projection: 553 instead of 350
+// TFLOP/s; a 256-token batch: 161 instead of 108) and loses otherwise (the Llama shard: 950
+// instead of 1210).
+inline int64_t tile_cost(int64_t M, int64_t N, int bm, int bn, int per_cu = 1, int rate_pct = 100)
 {
     const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
-    return ceil_div(tiles, compute_units()) * bm * bn;
+    return ceil_div(tiles, (int64_t)compute_units() * per_cu) * bm * bn * 100 / rate_pct;
 }
 
 // The direct-to-LDS kernel loads whole 16-byte chunks and addresses a tile with 32-bit byte
@@ -79,17 +88,20 @@ inline void run_bf16(const void* A, const void* B, int64_t M, int64_t N, int64_t
     if (dma_eligible(A_KC, B_KC, M, N, K, lda, ldb)) {
         // Candidates in order of preference (larger tiles first); the first of the lowest cost
         // wins. The narrower tiles only where they divide the extent exactly.
-        const int64_t cost[4] = {tile_cost(M, N, 256, 256),
-                                 (N % 224 == 0) ? tile_cost(M, N, 256, 224) : INT64_MAX,
-                                 (M % 224 == 0) ? tile_cost(M, N, 224, 256) : INT64_MAX,
-                                 (N % 192 == 0) ? tile_cost(M, N, 256, 192) : INT64_MAX};
+        constexpr int kCands = 5;
+        const int64_t cost[kCands] = {tile_cost(M, N, 256, 256),
+                                      (N % 224 == 0) ? tile_cost(M, N, 256, 224) : INT64_MAX,
+                                      (M % 224 == 0) ? tile_cost(M, N, 224, 256) : INT64_MAX,
+                                      (N % 192 == 0) ? tile_cost(M, N, 256, 192) : INT64_MAX,
+                                      tile_cost(M, N, 128, 128, 2, 42)};
         int best = 0;
-        for (int c = 1; c < 4; ++c)
+        for (int c = 1; c < kCands; ++c)
             if (cost[c] < cost[best]) best = c;
         switch (best) {
         case 1: run_dma<DmaTile256x224, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
         case 2: run_dma<DmaTile224x256, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
         case 3: run_dma<DmaTile256x192, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
+        case 4: run_dma<DmaTile128x128, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
         default: run_dma<DmaTile256x256, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
         }
     } else

@@ -37,6 +37,9 @@ struct DmaTile {
     static constexpr int GROUP_M = GROUP_M_;
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    // Waves per SIMD the kernel must leave room for: a 4-wave tile asks for 2, so that two
+    // workgroups (and their two LDS double buffers) can share a CU.
+    static constexpr int MIN_WAVES_PER_SIMD = NWAVES >= 8 ? 1 : 2;
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "tiles move in 1 KB wave loads");
     static_assert(2 * STAGE_BYTES <= 160 * 1024, "two stages must fit in LDS");
@@ -333,7 +336,7 @@ struct EpiIsDual<E, std::void_t<decltype(E::kDual)>> : std::bool_constant<E::kDu
 // C[M, N] = A B, or in the dual form the pair (A B, A B2) handed to epi.apply_dual: one A tile
 // in LDS feeds both products, as the gated MLP's gate and up projections need [Z 08].
 template <class Cfg, bool A_KC, bool B_KC, class Epi>
-__global__ __launch_bounds__(Cfg::NTHREADS, 1) void gemm_bf16_dma(
+__global__ __launch_bounds__(Cfg::NTHREADS, Cfg::MIN_WAVES_PER_SIMD) void gemm_bf16_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const uint16_t* __restrict__ B2, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
     Epi epi)

@@ -230,10 +230,18 @@ RAGGED = [
     # no biases
     Workload("nobias_n128_d128_f256_t2", 128, 128, 256, 2, "gelu_tanh", "bf16", 7007, "normal",
              bias=False),
-    # widths that are multiples of 224: the 256x224 and 224x256 tiles, with a ragged token tail
-    Workload("tile224_n300_d448_f896_t2", 300, 448, 896, 2, "gelu_tanh", "bf16", 7008, "normal"),
-    # widths that are multiples of 192: the 256x192 tile (both weight layouts in the backward)
-    Workload("tile192_n300_d384_f768_t2", 300, 384, 768, 2, "gelu_tanh", "bf16", 7009, "normal"),
+    # Shapes that fill the GPU with the large tiles (small ones take the 128 x 128 tile); a short
+    # contraction keeps the oracle cheap, and D = 72 is one full and one partial k stage.
+    # up-projection and dH on 256 x 224 (Fs = 16 x 224, 256 tiles)
+    Workload("tile224_n4096_d72_f3584_t1", 4096, 72, 3584, 1, "gelu_tanh", "bf16", 7008, "normal"),
+    # up-projection on 256 x 192 (Fs = 32 x 192, 256 tiles)
+    Workload("tile192_n2048_d72_f6144_t1", 2048, 72, 6144, 1, "gelu_tanh", "bf16", 7009, "normal"),
+    # down-projection and dX on 256 x 256 (256 tiles)
+    Workload("tile256_n4096_d4096_f64_t1", 4096, 4096, 64, 1, "gelu_tanh", "bf16", 7012,
+             "normal"),
+    # down-projection on 224 x 256 (N = 16 x 224 tokens, 256 tiles)
+    Workload("tile224m_n3584_d4096_f64_t1", 3584, 4096, 64, 1, "gelu_tanh", "bf16", 7013,
+             "normal"),
     # contraction shorter than one 64-deep stage (K = 40 up, 48 down): one partial stage
     Workload("kshort_n130_d40_f96_t2", 130, 40, 96, 2, "gelu_tanh", "bf16", 7010, "normal"),
     # contraction of exactly one stage (K = 64 both ways)
