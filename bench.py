@@ -37,7 +37,8 @@ WARMUP_MS = 250.0      # headline: from idle the clocks settle after ~40 ms of l
 ROW_WARMUP_MS = 150.0  # each extra row, after its own input set-up
 
 ROWS = ("fwd_cold_operands", "partial_reduce", "shard_bwd", "sum_dx", "gated_shard_fwd",
-        "gated_shard_bwd", "gpt3_layer", "reduce_scatter_slice", "shard_count_sweep")
+        "gated_shard_bwd", "gpt3_layer", "reduce_scatter_slice", "shard_count_sweep",
+        "gpt2_medium_block")
 
 
 def log(msg: str) -> None:
@@ -388,7 +389,39 @@ def measure_next_rows(torch, mt, synth, workloads, dev, g, want=ROWS):
         res.update(_rows_gpt3_layer(torch, mt, workloads, dev, g, want))
     if "shard_count_sweep" in want:
         res.update(_row_t_sweep(torch, mt, workloads, dev, g))
+    if "gpt2_medium_block" in want:
+        res.update(_row_gpt2_medium(torch, mt, workloads, dev, g))
     return res
+
+
+def _row_gpt2_medium(torch, mt, workloads, dev, g):
+    """The GPT-2-medium-shaped block (N=4096, D=1024, F=4096, T=2) on one GPU: both shards'
+    forward, then the 2-way tail with b2. Its products are too small for the 256-wide tiles to
+    fill the GPU, so they take the 128 x 128 tile."""
+    w = workloads.GPT2_MEDIUM_T2
+    N, D, F, T, Fs = w.N, w.D, w.F, w.T, w.Fs
+    X = _randn_bf16(torch, (N, D), 1.0, g, dev)
+    W1s = [_randn_bf16(torch, (D, Fs), 0.02, g, dev) for _ in range(T)]
+    b1s = [_randn_bf16(torch, (Fs,), 0.02, g, dev) for _ in range(T)]
+    W2s = [_randn_bf16(torch, (Fs, D), 0.02, g, dev) for _ in range(T)]
+    b2 = _randn_bf16(torch, (D,), 0.02, g, dev)
+    H = torch.empty((N, Fs), dtype=torch.bfloat16, device=dev)
+    parts = [torch.empty((N, D), device=dev) for _ in range(T)]
+    Y = torch.empty((N, D), device=dev)
+
+    def block():
+        for r in range(T):
+            mt.mlp_tp_shard_fwd(X, W1s[r], b1s[r], W2s[r], H, None, parts[r], N, D, F, T, mt.BF16,
+                                w.act)
+        mt.mlp_tp_partial_reduce(parts, T, b2, mt.BF16, Y, N, D)
+
+    ms = _time_loop(torch, block, 50)
+    flop = 4.0 * N * D * F
+    out = {"workload": w.name, "ms": round(ms, 5), "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1),
+           "frac_mfma": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    log(f"[bench] gpt2-medium block (2 shards + tail): {ms:.4f} ms, {out['TFLOP/s']} TFLOP/s")
+    del X, W1s, b1s, W2s, b2, H, parts, Y
+    return {"gpt2_medium_block": out}
 
 
 def _row_gated(torch, mt, workloads, dev, g, want):
