@@ -40,6 +40,12 @@ struct DmaTile {
     // Waves per SIMD the kernel must leave room for: a 4-wave tile asks for 2, so that two
     // workgroups (and their two LDS double buffers) can share a CU.
     static constexpr int MIN_WAVES_PER_SIMD = NWAVES >= 8 ? 1 : 2;
+    // Who issues a stage's global->LDS loads, and when. On the 256 x 224 and 256 x 192 tiles,
+    // waves 0-3 (one per SIMD) issue all of them at the start of the stage while their SIMD
+    // partners, waves 4-7, keep the matrix cores busy: +4% and up to +2% against every wave
+    // issuing its share spread over the stage, which the 256 x 256 tile keeps (-2% otherwise).
+    static constexpr bool LOADERS_UP_FRONT = NWAVES == 8 && BM == 256 && BN < 256;
+    static constexpr int NLOAD = LOADERS_UP_FRONT ? 4 : NWAVES;  // waves that issue loads
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "tiles move in 1 KB wave loads");
     static_assert(2 * STAGE_BYTES <= 160 * 1024, "two stages must fit in LDS");
@@ -74,7 +80,8 @@ __device__ __forceinline__ int mc_swz(int k)
         return (k & 3) << 1;
 }
 
-// Issues load q of this wave's share of the global->LDS copy of one operand tile (ROWS x 64 k).
+// Issues load q of this wave's share of the global->LDS copy of one operand tile (ROWS x 64 k),
+// shared among NLOAD waves (wave < NLOAD).
 //   KC: element (row, k) at src[row * ld + k]; LDS [ROWS][64].
 //   MC: element (row, k) at src[k * ld + row]; LDS [64][ROWS].
 // `src` already points at (row0, k0); rows >= rows_left or k >= k_left load zeros. One buffer
@@ -82,14 +89,14 @@ __device__ __forceinline__ int mc_swz(int k)
 // scalar offset operand, so the per-lane offset only holds the row within the load and the
 // swizzled chunk. (Out-of-range lanes carry an offset of 2^31 in the vector operand, past the
 // resource's range whether or not the hardware adds the scalar offset before its check.)
-template <int ROWS, int NWAVES, bool KC>
+template <int ROWS, int NLOAD, bool KC>
 __device__ __forceinline__ void dma_load_one(const uint16_t* src, int64_t ld, int rows_left,
                                              int k_left, MLPTP_LDS uint8_t* lds, int wave, int lane,
                                              int q)
 {
     constexpr int kInstr = ROWS * 64 * 2 / 1024;  // 1 KB wave loads per tile
-    const int qi = q * NWAVES + wave;
-    if (kInstr % NWAVES != 0 && qi >= kInstr) return;  // wave-uniform
+    const int qi = q * NLOAD + wave;
+    if (kInstr % NLOAD != 0 && qi >= kInstr) return;  // wave-uniform
     const i32x4 rsrc = make_buffer_rsrc(src);
     int off;
     int first;  // first row (KC) or k row (MC) of this load
@@ -183,31 +190,31 @@ __device__ __forceinline__ StageSrc stage_src(const DmaCtx& c, int64_t kt)
 // Loads per wave for a whole stage: the A tile's, then the B tile's (both halves in the dual form).
 template <class Cfg, bool DUAL>
 struct StageLoads {
-    static constexpr int QA = dma_loads_per_wave<Cfg::BM, Cfg::NWAVES>();
-    static constexpr int QH = dma_loads_per_wave<Cfg::BN / 2, Cfg::NWAVES>();
-    static constexpr int QB = DUAL ? 2 * QH : dma_loads_per_wave<Cfg::BN, Cfg::NWAVES>();
+    static constexpr int QA = dma_loads_per_wave<Cfg::BM, Cfg::NLOAD>();
+    static constexpr int QH = dma_loads_per_wave<Cfg::BN / 2, Cfg::NLOAD>();
+    static constexpr int QB = DUAL ? 2 * QH : dma_loads_per_wave<Cfg::BN, Cfg::NLOAD>();
     static constexpr int Q = QA + QB;
 };
 
-// Load q (0 <= q < StageLoads::Q) of this wave's share of a stage.
+// Load q (0 <= q < StageLoads::Q) of this wave's share of a stage (waves below Cfg::NLOAD).
 template <class Cfg, bool A_KC, bool B_KC, bool DUAL>
 __device__ __forceinline__ void stage_load(const DmaCtx& c, const StageSrc& t,
                                            MLPTP_LDS uint8_t* base, int q)
 {
     using SL = StageLoads<Cfg, DUAL>;
     if (q < SL::QA) {
-        dma_load_one<Cfg::BM, Cfg::NWAVES, A_KC>(t.a, c.lda, c.m_left, t.k_left, base, c.wave,
+        dma_load_one<Cfg::BM, Cfg::NLOAD, A_KC>(t.a, c.lda, c.m_left, t.k_left, base, c.wave,
                                                  c.lane, q);
     } else if constexpr (!DUAL) {
-        dma_load_one<Cfg::BN, Cfg::NWAVES, B_KC>(t.b, c.ldb, c.n_left, t.k_left,
+        dma_load_one<Cfg::BN, Cfg::NLOAD, B_KC>(t.b, c.ldb, c.n_left, t.k_left,
                                                  base + Cfg::A_BYTES, c.wave, c.lane, q - SL::QA);
     } else {
         constexpr int HB = Cfg::BN / 2;
         if (q < SL::QA + SL::QH)
-            dma_load_one<HB, Cfg::NWAVES, B_KC>(t.b, c.ldb, c.n_left, t.k_left,
+            dma_load_one<HB, Cfg::NLOAD, B_KC>(t.b, c.ldb, c.n_left, t.k_left,
                                                 base + Cfg::A_BYTES, c.wave, c.lane, q - SL::QA);
         else
-            dma_load_one<HB, Cfg::NWAVES, B_KC>(t.b2, c.ldb, c.n_left, t.k_left,
+            dma_load_one<HB, Cfg::NLOAD, B_KC>(t.b2, c.ldb, c.n_left, t.k_left,
                                                 base + Cfg::A_BYTES + Cfg::B_BYTES / 2, c.wave,
                                                 c.lane, q - SL::QA - SL::QH);
     }
@@ -218,6 +225,7 @@ template <class Cfg, bool A_KC, bool B_KC, bool DUAL>
 __device__ __forceinline__ void dma_issue(const DmaCtx& c, int64_t kt, MLPTP_LDS uint8_t* base)
 {
     const StageSrc t = stage_src<Cfg, A_KC, B_KC, DUAL>(c, kt);
+    if (c.wave >= Cfg::NLOAD) return;
 #pragma unroll
     for (int q = 0; q < StageLoads<Cfg, DUAL>::Q; ++q) stage_load<Cfg, A_KC, B_KC, DUAL>(c, t, base, q);
 }
@@ -269,18 +277,22 @@ __device__ __attribute__((always_inline)) inline void dma_step(
             bfr[f] = B_KC ? frag_kc<HB>(Bh, row, ks, c.lane) : frag_mc<HB>(Bh, row, ks, c.lane);
         }
     };
-    // Placement of the next stage's loads: kPerGroup after each MFMA group, from the first. With
-    // a transposed A (the weight-gradient products, whose strided operand loads take longer) two
-    // per group, so they are all in flight within the first half of the stage. Measured on the
-    // bench's rows against loads all up front: one per group was +1-2% on the forward, two per
-    // group +2% on the GPT-3-175B layer's 256x192 tiles, and either was within 1% on the rest.
-    constexpr int kUpFront = 0, kPerGroup = A_KC ? 1 : 2;
+    // Placement of the next stage's loads. With loader waves (Cfg::LOADERS_UP_FRONT) all of them
+    // before the stage's first reads. Otherwise kPerGroup after each MFMA group, from the first;
+    // with a transposed A (the weight-gradient products, whose strided operand loads take longer)
+    // two per group, so they are all in flight within the first half of the stage. Measured on
+    // the bench's rows against loads all up front: one per group was +1-2% on the forward, two
+    // per group +2% on the GPT-3-175B layer, and either was within 1% on the rest.
+    constexpr int kUpFront = Cfg::LOADERS_UP_FRONT ? SL::Q : 0;
+    constexpr int kPerGroup = Cfg::LOADERS_UP_FRONT ? 0 : (A_KC ? 1 : 2);
+    const bool loader = c.wave < Cfg::NLOAD;
     // A scheduling barrier closes each group: without it the compiler, knowing the loads do not
     // alias the reads, sank all of a 256x192 tile's loads to the end of the stage, in front of the
     // wait for them (the GPT-3-175B layer ran 20% slower).
     constexpr bool kPin = true;
 #pragma unroll
-    for (int q = 0; q < kUpFront && q < SL::Q; ++q) stage_load<Cfg, A_KC, B_KC, DUAL>(c, src, nxt, q);
+    for (int q = 0; q < kUpFront && q < SL::Q; ++q)
+        if (loader) stage_load<Cfg, A_KC, B_KC, DUAL>(c, src, nxt, q);
     // B fragment 0 first: the first MFMA needs it and A fragment 0 only (3 reads, not 6).
     read_b(0);
     read_a(0);
@@ -295,7 +307,7 @@ __device__ __attribute__((always_inline)) inline void dma_step(
 #pragma unroll
         for (int u = 0; u < kPerGroup; ++u) {
             const int q = kUpFront + g * kPerGroup + u;
-            if (q < SL::Q) stage_load<Cfg, A_KC, B_KC, DUAL>(c, src, nxt, q);
+            if (q < SL::Q && loader) stage_load<Cfg, A_KC, B_KC, DUAL>(c, src, nxt, q);
         }
         const int f = g + L;
         if (f < G) {
@@ -306,7 +318,7 @@ __device__ __attribute__((always_inline)) inline void dma_step(
     }
 #pragma unroll
     for (int q = kUpFront + G * kPerGroup; q < SL::Q; ++q)
-        stage_load<Cfg, A_KC, B_KC, DUAL>(c, src, nxt, q);
+        if (loader) stage_load<Cfg, A_KC, B_KC, DUAL>(c, src, nxt, q);
 }
 
 // For a pair of accumulator fragments a (columns c..c+15) and b (columns c+16..c+31) of the
