@@ -38,7 +38,7 @@ ROW_WARMUP_MS = 150.0  # each extra row, after its own input set-up
 
 ROWS = ("fwd_cold_operands", "partial_reduce", "shard_bwd", "sum_dx", "gated_shard_fwd",
         "gated_shard_bwd", "gpt3_layer", "reduce_scatter_slice", "shard_count_sweep",
-        "gpt2_medium_block")
+        "gpt2_medium_block", "epilogue_fusion_ablation")
 
 
 def log(msg: str) -> None:
@@ -152,6 +152,8 @@ def main() -> int:
     up_ms = [e[0].elapsed_time(e[1]) for e in ev]
     down_ms = [e[1].elapsed_time(e[2]) for e in ev]
     ms_per_step = total_ms / K
+    step_ms = sorted(u + d for u, d in zip(up_ms, down_ms))
+    median_ms = step_ms[K // 2] if K % 2 else 0.5 * (step_ms[K // 2 - 1] + step_ms[K // 2])
     gemm_flop = 2.0 * N * D * Fs
     fwd_flop = 2.0 * gemm_flop
     value = fwd_flop / (ms_per_step * 1e-3) / 1e12
@@ -201,6 +203,8 @@ def main() -> int:
         "warmup": warm_steps,
         "warmup_ms": round(warm_ms, 1),
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_median": round(median_ms, 5),
+        "ms_per_step_min": round(step_ms[0], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -213,6 +217,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "rows": rows,
         "device": torch.cuda.get_device_name(dev),
+        "hip": getattr(torch.version, "hip", None),
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -263,6 +268,8 @@ def measure_rows(torch, mt, synth, workloads, dev, X, W1, b1, W2, H, w, want=ROW
     g.manual_seed(1234)
     if "fwd_cold_operands" in want:
         res.update(_row_cold(torch, mt, dev, X, W1, b1, W2, H, w))
+    if "epilogue_fusion_ablation" in want:
+        res.update(_row_fusion_ablation(torch, mt, dev, X, W1, b1, H, w))
     if "partial_reduce" in want:
         res.update(_row_partial_reduce(torch, mt, synth, workloads, dev, g))
     if "shard_bwd" in want or "sum_dx" in want:
@@ -310,6 +317,42 @@ def _row_cold(torch, mt, dev, X, W1, b1, W2, H, w, copies=3):
         f"{out['TFLOP/s']} TFLOP/s")
     del sets, P
     return {"fwd_cold_operands": out}
+
+
+def _row_fusion_ablation(torch, mt, dev, X, W1, b1, H, w):
+    """What fusing bias + GELU into the up-projection's GEMM saves: the fused launch against the
+    same GEMM writing its fp32 result, then the epilogue as a kernel of its own (which reads that
+    result back from HBM and writes H)."""
+    N, D, F, T, Fs = w.N, w.D, w.F, w.T, w.Fs
+    Z32 = torch.empty((N, Fs), device=dev)
+
+    def fused():
+        mt.mlp_tp_up_proj(X, W1, b1, None, H, N, D, F, T, mt.BF16, w.act)
+
+    def gemm_only():
+        # P[N, D'] = X[N, F'] W1^(r)[F', D'] with D' = Fs, F' = D, T' = 1: the up-projection's
+        # product, written as fp32
+        mt.mlp_tp_down_proj(X, W1, Z32, N, Fs, D, 1, mt.BF16)
+
+    def epilogue_only():
+        mt.mlp_tp_bias_act(Z32, b1, H, N, F, T, mt.BF16, w.act)
+
+    ms_f = _time_loop(torch, fused, 50)
+    ms_g = _time_loop(torch, gemm_only, 50)
+    ms_e = _time_loop(torch, epilogue_only, 50)
+    ep_bytes = N * Fs * (4 + 2) + Fs * 2
+    flop = 2.0 * N * D * Fs
+    out = {"workload": w.name, "fused_ms": round(ms_f, 5), "gemm_fp32_out_ms": round(ms_g, 5),
+           "standalone_epilogue_ms": round(ms_e, 5), "unfused_ms": round(ms_g + ms_e, 5),
+           "fused_TFLOP/s": round(flop / (ms_f * 1e-3) / 1e12, 1),
+           "unfused_TFLOP/s": round(flop / ((ms_g + ms_e) * 1e-3) / 1e12, 1),
+           "standalone_epilogue_GB/s": round(ep_bytes / (ms_e * 1e-3) / 1e9, 1),
+           "standalone_epilogue_frac_hbm": round(ep_bytes / (ms_e * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "standalone_epilogue_bytes": ep_bytes}
+    log(f"[bench] epilogue fusion: fused {ms_f:.4f} ms | GEMM to fp32 {ms_g:.4f} + epilogue "
+        f"{ms_e:.4f} ms ({out['standalone_epilogue_GB/s']} GB/s)")
+    del Z32
+    return {"epilogue_fusion_ablation": out}
 
 
 def _row_partial_reduce(torch, mt, synth, workloads, dev, g):

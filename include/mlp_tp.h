@@ -281,6 +281,20 @@ int mlp_tp_swiglu_shard_bwd(const void* X, const void* Wgr, const void* Wur, con
                             int64_t N, int64_t D, int64_t F, int32_t T, int32_t dtype,
                             void* stream);
 
+/*
+ * The up-projection's epilogue on its own [Z 02], [Z 05]: H = phi(Z + b1r) for a shard's
+ * fp32 pre-activation, the same arithmetic the fused up-projection applies to its GEMM result
+ * (bias add in fp32, phi, one rounding to dtype). For a pre-activation computed elsewhere, and
+ * as the unfused reference that shows what the fusion saves.
+ *   Z    [N, Fs] float, row-major, Fs = F / T.
+ *   b1r  [Fs] dtype, the bias slice; NULL for no bias.
+ *   H    [N, Fs] dtype output.
+ * Errors: E_NULL (Z, H), E_SHAPE, E_INDIVISIBLE, E_DTYPE, E_ACT, E_ALIGN, E_ALIAS (H overlapping
+ * Z or b1r), E_HIP. N = 0 is a no-op.
+ */
+int mlp_tp_bias_act(const float* Z, const void* b1r, void* H, int64_t N, int64_t F, int32_t T,
+                    int32_t dtype, int32_t act, void* stream);
+
 /* Static description of a return code; never NULL. */
 const char* mlp_tp_strerror(int code);
 

@@ -64,6 +64,7 @@ def load() -> ctypes.CDLL:
         "mlp_tp_swiglu_shard_fwd": ([vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
                                      vp], ctypes.c_int),
         "mlp_tp_swiglu_shard_bwd": ([vp] * 14 + [i64, i64, i64, i32, i32, vp], ctypes.c_int),
+        "mlp_tp_bias_act": ([vp, vp, vp, i64, i64, i32, i32, i32, vp], ctypes.c_int),
         "mlp_tp_strerror": ([ctypes.c_int], ctypes.c_char_p),
     }
     for name, (args, res) in sigs.items():
@@ -211,6 +212,12 @@ def mlp_tp_swiglu_shard_bwd(X, Wgr, Wur, W2r, G, U, H, dY, dG, dU, dWgr, dWur, d
                                         _ptr(dWur), _ptr(dW2r), _ptr(dXr), N, D, F, T, dtype,
                                         _stream(stream))
     return _check(rc, "mlp_tp_swiglu_shard_bwd")
+
+
+def mlp_tp_bias_act(Z, b1r, H, N, F, T, dtype, act, stream=None):
+    rc = load().mlp_tp_bias_act(_ptr(Z), _ptr(b1r), _ptr(H), N, F, T, dtype, _act(act),
+                                _stream(stream))
+    return _check(rc, "mlp_tp_bias_act")
 
 
 def mlp_tp_strerror(code: int) -> str:

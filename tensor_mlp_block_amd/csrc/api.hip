@@ -449,6 +449,22 @@ int mlp_tp_swiglu_shard_bwd(const void* X, const void* Wgr, const void* Wur, con
     return launch_status();
 }
 
+int mlp_tp_bias_act(const float* Z, const void* b1r, void* H, int64_t N, int64_t F, int32_t T,
+                    int32_t dtype, int32_t act, void* stream)
+{
+    if (!Z || !H) return MLP_TP_E_NULL;
+    // D does not enter; 1 stands in for it in the shared shape check.
+    if (int rc = check_shard_shape(N, 1, F, T)) return rc;
+    if (!dtype_ok(dtype)) return MLP_TP_E_DTYPE;
+    if (!act_ok(act)) return MLP_TP_E_ACT;
+    if (int rc = all_aligned({Z, b1r, H})) return rc;
+    const int64_t es = elem_size(dtype), Fs = F / T;
+    if (int rc = disjoint({{H, N * Fs * es}}, {{Z, N * Fs * 4}, {b1r, Fs * es}})) return rc;
+    if (N == 0) return MLP_TP_OK;
+    mlptp::launch_bias_act(Z, b1r, H, N, Fs, dtype, act, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
 const char* mlp_tp_strerror(int code)
 {
     switch (code) {

@@ -1,0 +1,145 @@
+// elementwise.hip -- bias and activation over an fp32 pre-activation: the up-projection's
+// epilogue [Z 02], [Z 05] as a kernel of its own.
+//
+// Pages cited, as [tag section]:
+//   [Z] zwjcode.cn, "一层 MLP 太宽而放不下时怎样切？列并行、行并行与块尾归约"
+//
+// H = phi(Z + b1^(r)) over a shard's [N, Fs] block: b1^(r) is the bias slice that travels with
+// W1's columns [Z 05], and phi is elementwise, so each shard applies it to its own columns with
+// no exchange [Z 02]. The up-projection fuses exactly this into its GEMM; the standalone form
+// takes the GEMM's fp32 result from elsewhere. It is bound by HBM: 4 bytes read and 2 (bf16) or
+// 4 (fp32) written per element, plus the bias, which stays in cache.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mlptp {
+
+namespace {
+
+constexpr int kEwBlock = 256, kEwVecs = 4;
+
+template <class T>
+__device__ __forceinline__ f32x4 bias4_at(const T* b, int64_t c);
+template <>
+__device__ __forceinline__ f32x4 bias4_at<uint16_t>(const uint16_t* b, int64_t c)
+{
+    const uint2 w = *reinterpret_cast<const uint2*>(b + c);
+    return f32x4{bf16_bits_to_f32(w.x & 0xffffu), bf16_bits_to_f32(w.x >> 16),
+                 bf16_bits_to_f32(w.y & 0xffffu), bf16_bits_to_f32(w.y >> 16)};
+}
+template <>
+__device__ __forceinline__ f32x4 bias4_at<float>(const float* b, int64_t c)
+{
+    return *reinterpret_cast<const f32x4*>(b + c);
+}
+
+template <class T>
+__device__ __forceinline__ void store4_to(T* p, f32x4 v);
+template <>
+__device__ __forceinline__ void store4_to<uint16_t>(uint16_t* p, f32x4 v)
+{
+    uint2 w;
+    w.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+    w.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = w;
+}
+template <>
+__device__ __forceinline__ void store4_to<float>(float* p, f32x4 v)
+{
+    *reinterpret_cast<f32x4*>(p) = v;
+}
+
+template <class T>
+__device__ __forceinline__ float load1(const T* b, int64_t c);
+template <>
+__device__ __forceinline__ float load1<uint16_t>(const uint16_t* b, int64_t c) { return bf16_bits_to_f32(b[c]); }
+template <>
+__device__ __forceinline__ float load1<float>(const float* b, int64_t c) { return b[c]; }
+
+template <class T>
+__device__ __forceinline__ void store1(T* p, float v);
+template <>
+__device__ __forceinline__ void store1<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+template <>
+__device__ __forceinline__ void store1<float>(float* p, float v) { *p = v; }
+
+// Vector path (Fs % 4 == 0): four 16-byte vectors of Z per thread, kEwBlock apart, all loaded
+// before the first is processed; the 4 values of a vector share one bias row position.
+template <class T, int ACT>
+__global__ __launch_bounds__(kEwBlock) void bias_act_vec(const float* __restrict__ Z,
+                                                         const T* __restrict__ b,
+                                                         T* __restrict__ H, int64_t nvec,
+                                                         int64_t Fs, int64_t v0)
+{
+    const int64_t base = v0 + (int64_t)blockIdx.x * (kEwBlock * kEwVecs) + threadIdx.x;
+    f32x4 z[kEwVecs];
+#pragma unroll
+    for (int u = 0; u < kEwVecs; ++u) {
+        const int64_t v = base + u * kEwBlock;
+        z[u] = v < nvec ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Z) + v)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kEwVecs; ++u) {
+        const int64_t v = base + u * kEwBlock;
+        if (v >= nvec) continue;
+        f32x4 x = z[u];
+        if (b) x += bias4_at<T>(b, (v * 4) % Fs);
+        f32x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = act_fwd<ACT>(x[e]);
+        store4_to<T>(H + v * 4, h);
+    }
+}
+
+// Element path for Fs % 4 != 0.
+template <class T, int ACT>
+__global__ __launch_bounds__(256) void bias_act_scalar(const float* __restrict__ Z,
+                                                       const T* __restrict__ b,
+                                                       T* __restrict__ H, int64_t n, int64_t Fs)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
+        float x = Z[e];
+        if (b) x += load1<T>(b, e % Fs);
+        store1<T>(H + e, act_fwd<ACT>(x));
+    }
+}
+
+template <class T, int ACT>
+void launch_typed(const float* Z, const T* b, T* H, int64_t N, int64_t Fs, hipStream_t s)
+{
+    const int64_t n = N * Fs;
+    if (Fs % 4 == 0) {
+        const int64_t nvec = n / 4, per_group = (int64_t)kEwBlock * kEwVecs;
+        const int64_t max_launch = int64_t(1) << 30;
+        for (int64_t g0 = 0; g0 < ceil_div(nvec, per_group); g0 += max_launch) {
+            const int64_t groups = ceil_div(nvec, per_group) - g0;
+            hipLaunchKernelGGL((bias_act_vec<T, ACT>),
+                               dim3((uint32_t)(groups < max_launch ? groups : max_launch)),
+                               dim3(kEwBlock), 0, s, Z, b, H, nvec, Fs, g0 * per_group);
+        }
+    } else {
+        const int64_t groups = ceil_div(n, 256) < 4096 ? ceil_div(n, 256) : 4096;
+        hipLaunchKernelGGL((bias_act_scalar<T, ACT>), dim3((uint32_t)groups), dim3(256), 0, s, Z,
+                           b, H, n, Fs);
+    }
+}
+
+}  // namespace
+
+void launch_bias_act(const float* Z, const void* b1r, void* H, int64_t N, int64_t Fs, int dtype,
+                     int act, hipStream_t s)
+{
+    with_act(act, [&](auto a) {
+        constexpr int ACT = decltype(a)::value;
+        if (dtype == kBF16)
+            launch_typed<uint16_t, ACT>(Z, static_cast<const uint16_t*>(b1r),
+                                        static_cast<uint16_t*>(H), N, Fs, s);
+        else
+            launch_typed<float, ACT>(Z, static_cast<const float*>(b1r), static_cast<float*>(H), N,
+                                     Fs, s);
+    });
+}
+
+}  // namespace mlptp

@@ -57,6 +57,10 @@ int64_t colsum_workspace_bytes(int64_t N, int64_t Fs);
 void launch_colsum(const void* dZ, float* ws, float* db1, int64_t N, int64_t Fs, int dtype,
                    hipStream_t s);
 
+// H = phi(Z + b1r): Z [N, Fs] fp32, b1r [Fs] (dtype, nullable), H [N, Fs] dtype.
+void launch_bias_act(const float* Z, const void* b1r, void* H, int64_t N, int64_t Fs, int dtype,
+                     int act, hipStream_t s);
+
 // Y = ((P[0] + P[1]) + ...) + b2 over T fp32 [N, D] partials (P is a host array).
 void launch_partial_reduce(const float* const* P, int T, const void* b2, int b2_dtype, float* Y,
                            int64_t N, int64_t D, hipStream_t s);

@@ -237,6 +237,30 @@ def test_swiglu_shard_bwd_argument_checks(lib):
     assert _gbwd(lib, dWu=C) == mt.E_ALIAS            # two weight gradients on one buffer
 
 
+def _bias_act(lib, **kw):
+    a = dict(Z=A, b=B, H=C, N=4, F=16, T=2, dtype=mt.BF16, act=mt.ACT["gelu_tanh"])
+    a.update(kw)
+    return lib.mlp_tp_bias_act(a["Z"], a["b"], a["H"], a["N"], a["F"], a["T"], a["dtype"],
+                               a["act"], S)
+
+
+def test_bias_act_argument_checks(lib):
+    # The up-projection's epilogue on its own [Z 02], [Z 05].
+    assert _bias_act(lib, Z=None) == mt.E_NULL
+    assert _bias_act(lib, H=None) == mt.E_NULL
+    assert _bias_act(lib, N=-1) == mt.E_SHAPE
+    assert _bias_act(lib, T=0) == mt.E_SHAPE
+    assert _bias_act(lib, T=3) == mt.E_INDIVISIBLE
+    assert _bias_act(lib, dtype=7) == mt.E_DTYPE
+    assert _bias_act(lib, act=99) == mt.E_ACT
+    assert _bias_act(lib, H=C + 4) == mt.E_ALIGN
+    assert _bias_act(lib, b=B + 8) == mt.E_ALIGN
+    assert _bias_act(lib, H=A + 16) == mt.E_ALIAS   # H inside Z
+    assert _bias_act(lib, H=B) == mt.E_ALIAS        # H over the bias
+    assert _bias_act(lib, N=0) == mt.OK             # nothing to do, no launch
+    assert _bias_act(lib, N=0, b=None) == mt.OK
+
+
 def test_header_has_no_torch_or_hip_types():
     with open(mt.HEADER) as f:
         text = f.read()

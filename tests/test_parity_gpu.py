@@ -289,6 +289,45 @@ def test_huge_leading_dimension_takes_register_staged_kernel():
     assert_close("P", s.P, P)
 
 
+@pytest.mark.parametrize("act", ["identity", "relu", "gelu_tanh", "gelu_erf", "gelu_sigmoid"])
+@pytest.mark.parametrize("dtype,N,F,T,bias", [("bf16", 77, 200, 2, True), ("bf16", 33, 60, 2, True),
+                                              ("f32", 64, 96, 1, True), ("bf16", 50, 128, 4, False),
+                                              ("f32", 9, 30, 3, False)])
+def test_bias_act_matches_oracle(act, dtype, N, F, T, bias):
+    """The epilogue on its own [Z 02], [Z 05]: phi(Z + b1) against the oracle's phi in fp64 on the
+    same values. Fs = 100, 128 and 96 take the vector path, 30 and 10 the element path."""
+    Fs = F // T
+    g = torch.Generator().manual_seed(4000 + N + F)
+    Zc = torch.randn((N, Fs), generator=g) * 2.0
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    bc = (torch.randn((Fs,), generator=g) * 0.5).to(tdt) if bias else None
+    H = torch.empty((N, Fs), dtype=tdt, device="cuda")
+    mt.mlp_tp_bias_act(Zc.cuda(), bc.cuda() if bias else None, H, N, F, T,
+                       mt.BF16 if dtype == "bf16" else mt.F32, act)
+    torch.cuda.synchronize()
+    pre = Zc.double().numpy() + (bc.double().numpy() if bias else 0.0)
+    ref = oracle.act(act, pre)
+    assert_close(f"H ({act})", H, ref, TOL if dtype == "bf16" else 1e-5)
+
+
+def test_unfused_epilogue_equals_fused_up_projection():
+    """The same GEMM writing its fp32 result (the down-projection entry point on X and W1^(r)),
+    then the standalone epilogue, gives the fused up-projection's H bit for bit: the same fp32
+    sums, the same bias add, phi and rounding."""
+    w = Workload("unfused_n300_d520_f1552_t2", 300, 520, 1552, 2, "gelu_tanh", "bf16", 7020,
+                 "normal")
+    Xc = synth.gen_X(w)
+    X = Xc.cuda()
+    s = Shard(w, X, 0)
+    Z32 = torch.empty((w.N, w.Fs), device="cuda")
+    # P[N, D'] = H'[N, F'/T'] W2'[F'/T', D'] with H' = X, W2' = W1^(r): D' = Fs, F' = D, T' = 1.
+    mt.mlp_tp_down_proj(X, s.dW1, Z32, w.N, w.Fs, w.D, 1, mt.BF16)
+    H = torch.empty_like(s.H)
+    mt.mlp_tp_bias_act(Z32, s.db1, H, w.N, w.F, w.T, mt.BF16, w.act)
+    torch.cuda.synchronize()
+    assert torch.equal(H, s.H)
+
+
 @pytest.mark.parametrize("w", [x for x in RAGGED if x.act != "relu"], ids=lambda w: w.name)
 def test_backward_shard_elementwise(w):
     """ReLU backward on real-valued data is left to the exact integer test: there the sign of
