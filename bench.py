@@ -128,6 +128,8 @@ def main() -> int:
         mt.mlp_tp_up_proj(X, W1, b1, None, H, N, D, F, T, mt.BF16, w.act)
         mt.mlp_tp_down_proj(H, W2, P, N, D, F, T, mt.BF16)
 
+    global ROW_WARMUP_MS
+    ROW_WARMUP_MS = min(ROW_WARMUP_MS, args.warmup_ms)  # a shorter requested warmup applies to rows
     warm_steps, warm_ms = warm_up(torch, step, args.warmup, args.warmup_ms)
     log(f"[bench] warmup {warm_steps} steps, {warm_ms:.0f} ms")
 
