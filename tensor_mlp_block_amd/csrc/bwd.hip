@@ -85,10 +85,10 @@ void launch_dx_accumulate(const void* dZ, const void* W1r, float* dX, int64_t N,
         run_simt<true, true>(dZ, W1r, N, D, Fs, Fs, Fs, epi, s);
 }
 
-// db1^(r)[j] = sum over tokens of dZ[n, j]. Pass 1: each workgroup sums a 128-token slab of
-// 256 columns into ws[slab, :]; pass 2 adds the slabs in order. No atomics, so the result is
-// the same on every run.
-constexpr int kColsumRows = 128;
+// db1^(r)[j] = sum over tokens of dZ[n, j]. Pass 1: each workgroup sums a slab of kColsumRows
+// tokens of one column block into ws[slab, :]; pass 2 adds the slabs in a fixed order. No atomics,
+// so the result is the same on every run.
+constexpr int kColsumRows = 64;
 
 template <class T>
 __device__ __forceinline__ float as_f32(T v);
@@ -97,6 +97,70 @@ __device__ __forceinline__ float as_f32<uint16_t>(uint16_t v) { return bf16_bits
 template <>
 __device__ __forceinline__ float as_f32<float>(float v) { return v; }
 
+// Element e of a 16-byte vector of T.
+template <class T>
+__device__ __forceinline__ float vec_elem(const uint4& v, int e);
+template <>
+__device__ __forceinline__ float vec_elem<uint16_t>(const uint4& v, int e)
+{
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+template <>
+__device__ __forceinline__ float vec_elem<float>(const uint4& v, int e)
+{
+    const uint32_t w = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+    return __uint_as_float(w);
+}
+
+// Vector form, for rows that are whole 16-byte vectors (Fs a multiple of 16 / sizeof(T); the base
+// pointer is 16-byte aligned). 32 threads span a row of the column block (one vector each) and the
+// 8 groups of 32 take tokens r0 + g, r0 + g + 8, ...: every load instruction of a wave reads two
+// contiguous row runs, and all of a thread's loads are issued before its first add. The 8 group
+// sums of a column are then added in group order through LDS.
+template <class T>
+__global__ __launch_bounds__(256) void colsum_slabs_vec(const T* __restrict__ dZ,
+                                                        float* __restrict__ ws, int64_t N,
+                                                        int64_t Fs)
+{
+    constexpr int VEC = 16 / (int)sizeof(T);
+    constexpr int COLS = 32 * VEC;
+    constexpr int PER = kColsumRows / 8;
+    __shared__ float part[8][COLS];
+    const int tx = threadIdx.x & 31, g = threadIdx.x >> 5;
+    const int64_t c0 = (int64_t)blockIdx.x * COLS + tx * VEC;
+    const int64_t r0 = (int64_t)blockIdx.y * kColsumRows + g;
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    if (c0 < Fs) {
+        uint4 v[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int64_t r = r0 + 8 * i;
+            v[i] = r < N ? *reinterpret_cast<const uint4*>(dZ + r * Fs + c0) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] += vec_elem<T>(v[i], e);
+    }
+    // Column tx * VEC + e sits at part[g][e * 32 + tx], so the 32 lanes of a store hit 32 banks.
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) part[g][e * 32 + tx] = acc[e];
+    __syncthreads();
+    const int t = threadIdx.x;
+    const int64_t col = (int64_t)blockIdx.x * COLS + t;
+    if (t < COLS && col < Fs) {
+        const int idx = (t % VEC) * 32 + t / VEC;
+        float sum = part[0][idx];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) sum += part[j][idx];
+        ws[(int64_t)blockIdx.y * Fs + col] = sum;
+    }
+}
+
+// Element form, for any Fs: one column per thread, tokens in order.
 template <class T>
 __global__ __launch_bounds__(256) void colsum_slabs(const T* __restrict__ dZ, float* __restrict__ ws,
                                                     int64_t N, int64_t Fs)
@@ -110,15 +174,23 @@ __global__ __launch_bounds__(256) void colsum_slabs(const T* __restrict__ dZ, fl
     ws[(int64_t)blockIdx.y * Fs + col] = acc;
 }
 
+// Pass 2: 64 columns per workgroup; the 4 groups of 64 threads add slabs q, q + 4, q + 8, ... and
+// their 4 sums are added in group order.
 __global__ __launch_bounds__(256) void colsum_finish(const float* __restrict__ ws,
                                                      float* __restrict__ out, int64_t slabs,
                                                      int64_t Fs)
 {
-    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (col >= Fs) return;
+    __shared__ float part[4][64];
+    const int tx = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int64_t col = (int64_t)blockIdx.x * 64 + tx;
     float acc = 0.f;
-    for (int64_t b = 0; b < slabs; ++b) acc += ws[b * Fs + col];
-    out[col] = acc;
+    if (col < Fs) {
+#pragma unroll 8
+        for (int64_t b = q; b < slabs; b += 4) acc += ws[b * Fs + col];
+    }
+    part[q][tx] = acc;
+    __syncthreads();
+    if (q == 0 && col < Fs) out[col] = ((part[0][tx] + part[1][tx]) + part[2][tx]) + part[3][tx];
 }
 
 int64_t colsum_workspace_bytes(int64_t N, int64_t Fs)
@@ -130,16 +202,28 @@ void launch_colsum(const void* dZ, float* ws, float* db1, int64_t N, int64_t Fs,
                    hipStream_t s)
 {
     const int64_t slabs = ceil_div(N, kColsumRows);
-    const dim3 grid1((uint32_t)ceil_div(Fs, 256), (uint32_t)slabs);
-    if (slabs == 0)
-        ;  // no tokens: the finishing pass writes zeros
-    else if (dtype == kBF16)
-        hipLaunchKernelGGL(colsum_slabs<uint16_t>, grid1, dim3(256), 0, s,
-                           static_cast<const uint16_t*>(dZ), ws, N, Fs);
-    else
-        hipLaunchKernelGGL(colsum_slabs<float>, grid1, dim3(256), 0, s,
-                           static_cast<const float*>(dZ), ws, N, Fs);
-    hipLaunchKernelGGL(colsum_finish, dim3((uint32_t)ceil_div(Fs, 256)), dim3(256), 0, s, ws, db1,
+    const int64_t es = dtype == kBF16 ? 2 : 4;
+    const int64_t vec = 16 / es;
+    if (slabs == 0) {
+        // no tokens: the finishing pass writes zeros
+    } else if (Fs % vec == 0) {
+        const dim3 grid((uint32_t)ceil_div(Fs, 32 * vec), (uint32_t)slabs);
+        if (dtype == kBF16)
+            hipLaunchKernelGGL(colsum_slabs_vec<uint16_t>, grid, dim3(256), 0, s,
+                               static_cast<const uint16_t*>(dZ), ws, N, Fs);
+        else
+            hipLaunchKernelGGL(colsum_slabs_vec<float>, grid, dim3(256), 0, s,
+                               static_cast<const float*>(dZ), ws, N, Fs);
+    } else {
+        const dim3 grid((uint32_t)ceil_div(Fs, 256), (uint32_t)slabs);
+        if (dtype == kBF16)
+            hipLaunchKernelGGL(colsum_slabs<uint16_t>, grid, dim3(256), 0, s,
+                               static_cast<const uint16_t*>(dZ), ws, N, Fs);
+        else
+            hipLaunchKernelGGL(colsum_slabs<float>, grid, dim3(256), 0, s,
+                               static_cast<const float*>(dZ), ws, N, Fs);
+    }
+    hipLaunchKernelGGL(colsum_finish, dim3((uint32_t)ceil_div(Fs, 64)), dim3(256), 0, s, ws, db1,
                        slabs, Fs);
 }
 

@@ -177,10 +177,10 @@ def test_accumulate_and_gated_checks(lib):
 def test_workspace_query_uses_global_sizes(lib):
     """[C 先弄清楚]: a [8192, 32768] weight split 8 ways gives [8192, 4096] per card; the
     library derives Fs = F / T from the global F itself. The db1 workspace holds one fp32 row
-    of Fs per 128 tokens."""
-    assert lib.mlp_tp_shard_bwd_workspace_bytes(128, 8192, 32768, 8) == 4096 * 4
-    assert lib.mlp_tp_shard_bwd_workspace_bytes(4096, 8192, 28672, 8) == 32 * 3584 * 4
-    assert lib.mlp_tp_shard_bwd_workspace_bytes(300, 8, 16, 2) == 3 * 8 * 4
+    of Fs per 64 tokens."""
+    assert lib.mlp_tp_shard_bwd_workspace_bytes(128, 8192, 32768, 8) == 2 * 4096 * 4
+    assert lib.mlp_tp_shard_bwd_workspace_bytes(4096, 8192, 28672, 8) == 64 * 3584 * 4
+    assert lib.mlp_tp_shard_bwd_workspace_bytes(300, 8, 16, 2) == 5 * 8 * 4
     assert lib.mlp_tp_shard_bwd_workspace_bytes(0, 8, 16, 2) == 0
     assert lib.mlp_tp_shard_bwd_workspace_bytes(4, 8, 18, 4) == mt.E_INDIVISIBLE
     assert lib.mlp_tp_shard_bwd_workspace_bytes(4, 0, 16, 2) == mt.E_SHAPE
