@@ -149,6 +149,7 @@ def main() -> int:
         mt.mlp_tp_down_proj(H, W2, P, N, D, F, T, mt.BF16)
         ev[i][2].record(stream)
     t1.record(stream)
+    sclk_mhz = read_sclk_mhz(torch, dev)  # read while the timed steps run
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     up_ms = [e[0].elapsed_time(e[1]) for e in ev]
@@ -196,6 +197,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(Xc, W1c, b1c, W2c, w, args.cpu_seconds)
 
+    props = torch.cuda.get_device_properties(dev)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -219,10 +221,47 @@ def main() -> int:
         "cpu_baseline": cpu,
         "rows": rows,
         "device": torch.cuda.get_device_name(dev),
+        "arch": getattr(props, "gcnArchName", None),
+        "compute_units": props.multi_processor_count,
+        "sclk_mhz_during_timing": sclk_mhz,
         "hip": getattr(torch.version, "hip", None),
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def read_sclk_mhz(torch, dev):
+    """The shader clock the driver reports for this GPU (the DPM level marked '*'), or None.
+    The DRM card is matched to the device by its PCI address."""
+    import glob
+    props = torch.cuda.get_device_properties(dev)
+    bus, domain = getattr(props, "pci_bus_id", None), getattr(props, "pci_domain_id", None)
+    if bus is None:
+        return None
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            addr = os.path.basename(os.path.realpath(os.path.dirname(path)))  # "0000:75:00.0"
+            dom, b = addr.split(":")[:2]
+            if int(b, 16) != bus or (domain is not None and int(dom, 16) != domain):
+                continue
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return int(line.split(":")[1].strip().lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def warm_up(torch, fn, min_calls, min_ms, chunk=8):
@@ -627,7 +666,8 @@ def cpu_baseline(Xc, W1c, b1c, W2c, w, seconds):
     el = time.perf_counter() - t
     tflops = rows * per_row_flop / el / 1e12
     return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(el, 2),
+            "kind": "oracle", "seconds": round(el, 2), "cpu_model": cpu_model(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{rows} of {w.N} token rows of the {w.name} shard-0 forward "
                       f"(fp64 C oracle, OpenMP over rows)"}
 
