@@ -33,9 +33,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
     return __builtin_bit_cast(uint16_t, b);
 }
 
+// Two values rounded and packed by one v_cvt_pk_bf16_f32 (lo in bits 0-15). Written as
+// two scalar conversions joined by a shift and an or, the compiler emits four instructions.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Logistic function 1 / (1 + e^-x), stable at both ends (e^-x -> inf gives 0, -> 0 gives 1).
@@ -58,6 +63,9 @@ constexpr float kTanhCubic = 0.044715f;
 constexpr float kSigmoidScale = 1.702f;
 constexpr float kInvSqrt2 = 0.7071067811865476f;
 constexpr float kInvSqrt2Pi = 0.3989422804014327f;
+// -2 log2(e) sqrt(2/pi) and that times 0.044715: the GELU-tanh exponent in base 2.
+constexpr float kGeluExp2C1 = (float)(-2.0 * 1.4426950408889634 * 0.7978845608028654);
+constexpr float kGeluExp2C3 = (float)(-2.0 * 1.4426950408889634 * 0.7978845608028654 * 0.044715);
 
 // phi(z) [Z 02]: elementwise, so each shard applies it to its own columns with no exchange.
 // The activation is a compile-time parameter so a kernel inlines only its own form.
@@ -67,8 +75,11 @@ __device__ __forceinline__ float act_fwd(float z)
     if constexpr (ACT == kActRelu) {
         return z > 0.0f ? z : 0.0f;
     } else if constexpr (ACT == kActGeluTanh) {
-        const float u = kSqrt2OverPi * (z + kTanhCubic * z * z * z);
-        return z * sigmoidf_(2.0f * u);
+        // z sigmoid(2u) = z / (1 + 2^t), t = -2 log2(e) u = z (c1 + c3 z^2): the constants are
+        // folded so the exponent is one multiply-add and one multiply, and the power of two is
+        // the hardware's (v_exp_f32). z -> -inf gives 2^t = inf and -0; z -> +inf gives z.
+        const float t = z * fmaf(z * z, kGeluExp2C3, kGeluExp2C1);
+        return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
     } else if constexpr (ACT == kActGeluErf) {
         return 0.5f * z * (1.0f + erff(z * kInvSqrt2));
     } else if constexpr (ACT == kActGeluSigmoid) {
