@@ -489,7 +489,9 @@ def measure_next_rows(torch, mt, synth, workloads, dev, g, want=ROWS):
 def _row_gpt2_medium(torch, mt, workloads, dev, g):
     """The GPT-2-medium-shaped block (N=4096, D=1024, F=4096, T=2) on one GPU: both shards'
     forward, then the 2-way tail with b2. Its products are too small for the 256-wide tiles to
-    fill the GPU, so they take the 128 x 128 tile."""
+    fill the GPU, so they take the 128 x 128 tile. Timed two ways: the shards one after the other
+    on one stream, and the two shards on two streams (as two ranks would run them), joined
+    before the tail."""
     w = workloads.GPT2_MEDIUM_T2
     N, D, F, T, Fs = w.N, w.D, w.F, w.T, w.Fs
     X = _randn_bf16(torch, (N, D), 1.0, g, dev)
@@ -497,22 +499,43 @@ def _row_gpt2_medium(torch, mt, workloads, dev, g):
     b1s = [_randn_bf16(torch, (Fs,), 0.02, g, dev) for _ in range(T)]
     W2s = [_randn_bf16(torch, (Fs, D), 0.02, g, dev) for _ in range(T)]
     b2 = _randn_bf16(torch, (D,), 0.02, g, dev)
-    H = torch.empty((N, Fs), dtype=torch.bfloat16, device=dev)
+    Hs = [torch.empty((N, Fs), dtype=torch.bfloat16, device=dev) for _ in range(T)]
     parts = [torch.empty((N, D), device=dev) for _ in range(T)]
     Y = torch.empty((N, D), device=dev)
+    main = torch.cuda.current_stream()
+    side = [torch.cuda.Stream() for _ in range(T - 1)]  # default priority
+    fork = [torch.cuda.Event() for _ in range(T - 1)]
+    join = [torch.cuda.Event() for _ in range(T - 1)]
 
-    def block():
+    def block_one_stream():
         for r in range(T):
-            mt.mlp_tp_shard_fwd(X, W1s[r], b1s[r], W2s[r], H, None, parts[r], N, D, F, T, mt.BF16,
-                                w.act)
+            mt.mlp_tp_shard_fwd(X, W1s[r], b1s[r], W2s[r], Hs[r], None, parts[r], N, D, F, T,
+                                mt.BF16, w.act)
         mt.mlp_tp_partial_reduce(parts, T, b2, mt.BF16, Y, N, D)
 
-    ms = _time_loop(torch, block, 50)
+    def block_streams():
+        for r in range(1, T):
+            fork[r - 1].record(main)
+            side[r - 1].wait_event(fork[r - 1])
+            mt.mlp_tp_shard_fwd(X, W1s[r], b1s[r], W2s[r], Hs[r], None, parts[r], N, D, F, T,
+                                mt.BF16, w.act, stream=side[r - 1])
+            join[r - 1].record(side[r - 1])
+        mt.mlp_tp_shard_fwd(X, W1s[0], b1s[0], W2s[0], Hs[0], None, parts[0], N, D, F, T, mt.BF16,
+                            w.act, stream=main)
+        for e in join:
+            main.wait_event(e)
+        mt.mlp_tp_partial_reduce(parts, T, b2, mt.BF16, Y, N, D)
+
+    ms1 = _time_loop(torch, block_one_stream, 50)
+    ms = _time_loop(torch, block_streams, 50)
     flop = 4.0 * N * D * F
-    out = {"workload": w.name, "ms": round(ms, 5), "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1),
-           "frac_mfma": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    log(f"[bench] gpt2-medium block (2 shards + tail): {ms:.4f} ms, {out['TFLOP/s']} TFLOP/s")
-    del X, W1s, b1s, W2s, b2, H, parts, Y
+    tf = lambda t: round(flop / (t * 1e-3) / 1e12, 1)
+    out = {"workload": w.name, "ms": round(ms, 5), "TFLOP/s": tf(ms),
+           "frac_mfma": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "streams": T,
+           "one_stream_ms": round(ms1, 5), "one_stream_TFLOP/s": tf(ms1)}
+    log(f"[bench] gpt2-medium block (2 shards + tail): {ms:.4f} ms, {out['TFLOP/s']} TFLOP/s on "
+        f"{T} streams; one stream {ms1:.4f} ms")
+    del X, W1s, b1s, W2s, b2, Hs, parts, Y
     return {"gpt2_medium_block": out}
 
 
