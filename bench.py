@@ -84,6 +84,8 @@ def main() -> int:
                     help="comma-separated subset of the extra rows to time: " + ", ".join(ROWS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--cpu-row-seconds", type=float, default=3.0,
+                    help="target CPU time of each sampled oracle timing of the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy three times, as the "
                          "known-size reference for hardware byte counters")
@@ -201,8 +203,10 @@ def main() -> int:
         rows = measure_rows(torch, mt, synth, workloads, dev, X, W1, b1, W2, H, w, want)
 
     cpu = None
+    cpu_rows = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(Xc, W1c, b1c, W2c, w, args.cpu_seconds)
+        cpu_rows = cpu_baseline_rows(synth, workloads, args.cpu_row_seconds)
 
     props = torch.cuda.get_device_properties(dev)
     out = {
@@ -227,6 +231,7 @@ def main() -> int:
                    "act": w.act, "parallelism": "one rank's shard on 1 GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_rows": cpu_rows,
         "rows": rows,
         "device": torch.cuda.get_device_name(dev),
         "arch": getattr(props, "gcnArchName", None),
@@ -701,6 +706,86 @@ def cpu_baseline(Xc, W1c, b1c, W2c, w, seconds):
             "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{rows} of {w.N} token rows of the {w.name} shard-0 forward "
                       f"(fp64 C oracle, OpenMP over rows)"}
+
+
+def _oracle_rows_sample(run, N, seconds):
+    """Times run(idx) on a bounded, evenly spread sample of token rows: a calibration call on
+    one row per oracle thread sets the sample size for about `seconds` of CPU time. Returns
+    (rows, elapsed seconds)."""
+    import numpy as np
+    import oracle
+
+    cal = max(2, min(N, oracle.num_threads()))
+    t = time.perf_counter()
+    run(np.arange(cal))
+    dt = (time.perf_counter() - t) / cal
+    rows = int(max(cal, min(N, seconds / max(dt, 1e-6))))
+    idx = np.linspace(0, N - 1, rows).astype(np.int64)
+    t = time.perf_counter()
+    run(idx)
+    return rows, time.perf_counter() - t
+
+
+def cpu_baseline_rows(synth, workloads, seconds):
+    """The fp64 oracle, as it stands, timed on the other workloads: the GPT-2-medium block (both
+    shards and the tail, whole), one GPT-3-175B shard's forward and the Llama shard's backward
+    (token-row samples: every product's cost is linear in the rows), and the sum of 8 dX
+    partials (a row sample). Reported beside the GPU rows; not a target."""
+    import numpy as np
+    import oracle
+
+    out = {"cores": oracle.num_threads(), "kind": "oracle"}
+    # GPT-2-medium block: 2 shards + tail, all 4096 rows.
+    w = workloads.GPT2_MEDIUM_T2
+    X = synth.gen_X(w).double().numpy()
+    W1, b1, W2 = (t.double().numpy() for t in (synth.gen_W1(w), synth.gen_b1(w), synth.gen_W2(w)))
+    b2 = synth.gen_b2(w).double().numpy()
+    t = time.perf_counter()
+    oracle.block_fwd(X, W1, b1, W2, b2, w.T, act=w.act)
+    el = time.perf_counter() - t
+    flop = 4.0 * w.N * w.D * w.F
+    out["gpt2_medium_block"] = {"workload": w.name, "seconds": round(el, 2),
+                                "TFLOP/s": round(flop / el / 1e12, 6),
+                                "sample": "all 4096 token rows, both shards and the tail"}
+    log(f"[bench] cpu rows: gpt2 block {el:.2f} s")
+    # GPT-3-175B: shard 0's forward on a row sample.
+    w = workloads.GPT3_175B_T8
+    Fs = w.Fs
+    X = synth.gen_X(w).double().numpy()
+    W1, b1, W2 = (t.double().numpy() for t in (synth.gen_W1(w, 0, Fs), synth.gen_b1(w, 0, Fs),
+                                               synth.gen_W2(w, 0, Fs)))
+    rows, el = _oracle_rows_sample(lambda idx: oracle.shard_fwd(X[idx], W1, b1, W2, 1, 0,
+                                                                act=w.act), w.N, seconds)
+    out["gpt3_175b_shard_fwd"] = {"workload": w.name, "seconds": round(el, 2),
+                                  "TFLOP/s": round(rows * 4.0 * w.D * Fs / el / 1e12, 6),
+                                  "sample": f"{rows} of {w.N} token rows of shard 0's forward"}
+    log(f"[bench] cpu rows: gpt3 shard {rows} rows {el:.2f} s")
+    # Llama shard backward (dZ, dW1, db1, dW2, dX of shard 0) on a row sample.
+    w = workloads.LLAMA70B_SHARD_T8_BWD
+    Fs = w.Fs
+    X = synth.gen_X(w).double().numpy()
+    dY = synth.gen_dY(w).double().numpy()
+    W1, b1, W2 = (t.double().numpy() for t in (synth.gen_W1(w, 0, Fs), synth.gen_b1(w, 0, Fs),
+                                               synth.gen_W2(w, 0, Fs)))
+    rows, el = _oracle_rows_sample(lambda idx: oracle.shard_bwd(X[idx], W1, b1, W2, dY[idx], 1, 0,
+                                                                act=w.act), w.N, seconds)
+    out["llama3_70b_shard_bwd"] = {"workload": w.name, "seconds": round(el, 2),
+                                   "TFLOP/s": round(rows * 8.0 * w.D * Fs / el / 1e12, 6),
+                                   "sample": f"{rows} of {w.N} token rows of shard 0's backward "
+                                             "(the forward it needs is recomputed inside and not "
+                                             "counted)"}
+    log(f"[bench] cpu rows: llama bwd {rows} rows {el:.2f} s")
+    # Sum of 8 dX partials [4096, 8192] fp32, on a row sample.
+    rng = np.random.default_rng(505)
+    nr = 512
+    parts = [rng.standard_normal((nr, w.D)).astype(np.float32) for _ in range(8)]
+    t = time.perf_counter()
+    oracle.partial_sum(parts)
+    el = time.perf_counter() - t
+    out["sum_dx"] = {"workload": w.name, "seconds": round(el, 4),
+                     "GB/s": round(9 * nr * w.D * 4 / el / 1e9, 2),
+                     "sample": f"{nr} of {w.N} rows of the 8 fp32 partials"}
+    return out
 
 
 if __name__ == "__main__":
