@@ -310,6 +310,38 @@ def test_bias_act_matches_oracle(act, dtype, N, F, T, bias):
     assert_close(f"H ({act})", H, ref, TOL if dtype == "bf16" else 1e-5)
 
 
+@pytest.mark.parametrize("act", ["identity", "relu", "gelu_tanh", "gelu_erf", "gelu_sigmoid"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_activations_far_from_zero_and_at_zero(act, dtype):
+    """phi at pre-activations from -1e4 to 1e4, at +-0 and at tiny values, element by element
+    with a relative bound (the max-normalised error of the other tests would hide the small
+    outputs): the saturating GELU forms must give z far right and 0 far left, not inf or NaN,
+    and the erf form must not lose the small outputs of negative z to cancellation.
+    The bound is rtol |ref| + 1e-15: rtol is 1e-2 for bf16 storage and 1e-4 for fp32 (an
+    exponential of an argument near 70 carries about 70 fp32 epsilons of relative error), and
+    1e-15 covers the fp64 oracle's own absolute error where its 1 + erf or 1 + tanh cancels."""
+    mags = [0.0, 1e-30, 1e-8, 1e-3, 0.1, 0.5, 1.0, 2.0, 3.0, 5.0, 8.0, 12.0, 20.0, 50.0, 100.0,
+            1e3, 1e4]
+    vals = sorted({s * m for m in mags for s in (1.0, -1.0)} | {-0.0})
+    Fs = 8 * ((len(vals) + 7) // 8)
+    Zc = torch.zeros((4, Fs), dtype=torch.float32)
+    Zc[0, :len(vals)] = torch.tensor(vals, dtype=torch.float32)
+    Zc[1, :len(vals)] = torch.tensor(vals[::-1], dtype=torch.float32)
+    Zc[2] = Zc[0] * 0.75
+    Zc[3] = -Zc[1] * 1.5
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    H = torch.empty((4, Fs), dtype=tdt, device="cuda")
+    mt.mlp_tp_bias_act(Zc.cuda(), None, H, 4, Fs, 1, mt.BF16 if dtype == "bf16" else mt.F32, act)
+    torch.cuda.synchronize()
+    h = H.double().cpu().numpy()
+    ref = oracle.act(act, Zc.double().numpy())
+    assert np.all(np.isfinite(h)), f"{act}: non-finite outputs {h[~np.isfinite(h)]}"
+    rtol = 1e-2 if dtype == "bf16" else 1e-4
+    bad = np.abs(h - ref) > rtol * np.abs(ref) + 1e-15
+    assert not bad.any(), (f"{act} ({dtype}): z={Zc.double().numpy()[bad][:6]} "
+                           f"gpu={h[bad][:6]} ref={ref[bad][:6]}")
+
+
 def test_unfused_epilogue_equals_fused_up_projection():
     """The same GEMM writing its fp32 result (the down-projection entry point on X and W1^(r)),
     then the standalone epilogue, gives the fused up-projection's H bit for bit: the same fp32
