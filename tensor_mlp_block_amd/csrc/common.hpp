@@ -56,16 +56,21 @@ __device__ __forceinline__ float sigmoidf_(float x)
 __device__ __forceinline__ float silu_f(float z) { return z * sigmoidf_(z); }
 
 // GELU, tanh form: 0.5 z (1 + tanh(u)) with u = sqrt(2/pi) (z + 0.044715 z^3). Since
-// 0.5 (1 + tanh(u)) equals the logistic function at 2u, it is evaluated as z * sigmoid(2u),
-// which needs one exponential and saturates cleanly for large |z|.
-constexpr float kSqrt2OverPi = 0.7978845608028654f;
-constexpr float kTanhCubic = 0.044715f;
+// 0.5 (1 + tanh(u)) equals the logistic function at 2u, it is evaluated as z * sigmoid(2u)
+// = z / (1 + 2^t), t = -2 log2(e) u, which needs one exponential and saturates cleanly for
+// large |z|. The constants are kept in double and folded before rounding to float.
+constexpr double kSqrt2OverPiD = 0.7978845608028654;
+constexpr double kTanhCubicD = 0.044715;
+constexpr double kLog2eD = 1.4426950408889634;
+// -2 log2(e) sqrt(2/pi) and that times 0.044715: the GELU-tanh exponent in base 2.
+constexpr float kGeluExp2C1 = (float)(-2.0 * kLog2eD * kSqrt2OverPiD);
+constexpr float kGeluExp2C3 = (float)(-2.0 * kLog2eD * kSqrt2OverPiD * kTanhCubicD);
+// 2 sqrt(2/pi) and 2 sqrt(2/pi) 3 (0.044715): twice the derivative of the tanh argument.
+constexpr float kGeluDu2C1 = (float)(2.0 * kSqrt2OverPiD);
+constexpr float kGeluDu2C3 = (float)(2.0 * kSqrt2OverPiD * 3.0 * kTanhCubicD);
 constexpr float kSigmoidScale = 1.702f;
 constexpr float kInvSqrt2 = 0.7071067811865476f;
 constexpr float kInvSqrt2Pi = 0.3989422804014327f;
-// -2 log2(e) sqrt(2/pi) and that times 0.044715: the GELU-tanh exponent in base 2.
-constexpr float kGeluExp2C1 = (float)(-2.0 * 1.4426950408889634 * 0.7978845608028654);
-constexpr float kGeluExp2C3 = (float)(-2.0 * 1.4426950408889634 * 0.7978845608028654 * 0.044715);
 
 // phi(z) [Z 02]: elementwise, so each shard applies it to its own columns with no exchange.
 // The activation is a compile-time parameter so a kernel inlines only its own form.
@@ -99,11 +104,14 @@ __device__ __forceinline__ float act_grad(float z)
     if constexpr (ACT == kActRelu) {
         return z > 0.0f ? 1.0f : 0.0f;
     } else if constexpr (ACT == kActGeluTanh) {
-        // s = sigmoid(2u) = 0.5 (1 + tanh u); 0.5 (1 - tanh^2 u) = 2 s (1 - s).
-        const float u = kSqrt2OverPi * (z + kTanhCubic * z * z * z);
-        const float s = sigmoidf_(2.0f * u);
-        const float du = kSqrt2OverPi * (1.0f + 3.0f * kTanhCubic * z * z);
-        return s + z * 2.0f * s * (1.0f - s) * du;
+        // s = sigmoid(2u) = 0.5 (1 + tanh u) = 1 / (1 + 2^t) with t as in act_fwd, and
+        // 0.5 (1 - tanh^2 u) = 2 s (1 - s): phi' = s + z s (1 - s) (2 du), where
+        // 2 du = 2 sqrt(2/pi) (1 + 3 (0.044715) z^2) is one multiply-add of z^2.
+        const float z2 = z * z;
+        const float t = z * fmaf(z2, kGeluExp2C3, kGeluExp2C1);
+        const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+        const float du2 = fmaf(z2, kGeluDu2C3, kGeluDu2C1);
+        return fmaf(z * s * (1.0f - s), du2, s);
     } else if constexpr (ACT == kActGeluErf) {
         const float cdf = 0.5f * erfcf(-z * kInvSqrt2);
         return cdf + z * kInvSqrt2Pi * __expf(-0.5f * z * z);
