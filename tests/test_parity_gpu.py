@@ -342,6 +342,54 @@ def test_activations_far_from_zero_and_at_zero(act, dtype):
                            f"gpu={h[bad][:6]} ref={ref[bad][:6]}")
 
 
+@pytest.mark.parametrize("act", ["identity", "relu", "gelu_tanh", "gelu_erf", "gelu_sigmoid"])
+def test_activation_derivative_far_from_zero_and_at_zero(act):
+    """phi' through the backward's dH GEMM epilogue [Z 06], element by element: with W2^(r) the
+    identity and dY all ones, dH = 1 and the stored dZ is phi'(Z) rounded to bf16. Z spans -1e4
+    to 1e4 with +-0 and tiny values; all outputs finite, ReLU'(0) = 0, and each element within
+    1e-2 |ref| + atol(z). The fp64 oracle evaluates 1 + tanh(u), 1 - tanh(u)^2 and 1 - sigmoid
+    as written, which keep only an absolute ~1e-16 once they approach 0 (z near -7 for the tanh
+    form), and phi' multiplies that by z du; atol(z) = 4e-16 (1 + |z| max(du, 1.702)) + 1e-15
+    with du = sqrt(2/pi) (1 + 3 (0.044715) z^2) covers exactly that and nothing more."""
+    mags = [0.0, 1e-30, 1e-8, 1e-3, 0.1, 0.5, 1.0, 2.0, 3.0, 5.0, 8.0, 12.0, 20.0, 50.0, 100.0,
+            1e3, 1e4]
+    vals = sorted({s * m for m in mags for s in (1.0, -1.0)} | {-0.0})
+    N, Fs = 64, 64
+    D, F, T = Fs, Fs, 1
+    Zc = torch.zeros((N, Fs), dtype=torch.float32)
+    for r in range(N):
+        Zc[r, :len(vals)] = torch.tensor(vals, dtype=torch.float32) * (1.0 + 0.01 * r)
+    Zb = Zc.to(torch.bfloat16)
+    dev = "cuda"
+    Z = Zb.to(dev)
+    W2 = torch.eye(Fs, D, dtype=torch.bfloat16, device=dev)
+    dY = torch.ones((N, D), dtype=torch.bfloat16, device=dev)
+    X = torch.zeros((N, D), dtype=torch.bfloat16, device=dev)
+    W1 = torch.zeros((D, Fs), dtype=torch.bfloat16, device=dev)
+    H = torch.zeros((N, Fs), dtype=torch.bfloat16, device=dev)
+    dZ = torch.empty((N, Fs), dtype=torch.bfloat16, device=dev)
+    dW1 = torch.empty((D, Fs), device=dev)
+    dW2 = torch.empty((Fs, D), device=dev)
+    db1 = torch.empty((Fs,), device=dev)
+    dX = torch.empty((N, D), device=dev)
+    nb = mt.mlp_tp_shard_bwd_workspace_bytes(N, D, F, T)
+    ws = torch.empty((max(nb, 16),), dtype=torch.uint8, device=dev)
+    mt.mlp_tp_shard_bwd(X, W1, W2, Z, H, dY, dZ, dW1, db1, dW2, dX, ws, ws.numel(), N, D, F, T,
+                        mt.BF16, act)
+    torch.cuda.synchronize()
+    g = dZ.double().cpu().numpy()
+    z = Zb.double().numpy()
+    ref = oracle.act_deriv(act, z)
+    assert np.all(np.isfinite(g)), f"{act}: non-finite phi'"
+    du = np.sqrt(2.0 / np.pi) * (1.0 + 3.0 * 0.044715 * z * z)
+    atol = 4e-16 * (1.0 + np.abs(z) * np.maximum(du, 1.702)) + 1e-15
+    bad = np.abs(g - ref) > 1e-2 * np.abs(ref) + atol
+    assert not bad.any(), (f"{act}: z={Zb.double().numpy()[bad][:6]} gpu={g[bad][:6]} "
+                           f"ref={ref[bad][:6]}")
+    if act == "relu":
+        assert np.all(g[Zb.double().numpy() == 0.0] == 0.0)
+
+
 def test_unfused_epilogue_equals_fused_up_projection():
     """The same GEMM writing its fp32 result (the down-projection entry point on X and W1^(r)),
     then the standalone epilogue, gives the fused up-projection's H bit for bit: the same fp32
