@@ -38,10 +38,7 @@ __device__ __forceinline__ void store4_to(T* p, f32x4 v);
 template <>
 __device__ __forceinline__ void store4_to<uint16_t>(uint16_t* p, f32x4 v)
 {
-    uint2 w;
-    w.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-    w.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-    *reinterpret_cast<uint2*>(p) = w;
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 template <>
 __device__ __forceinline__ void store4_to<float>(float* p, f32x4 v)
@@ -64,14 +61,18 @@ template <>
 __device__ __forceinline__ void store1<float>(float* p, float v) { *p = v; }
 
 // Vector path (Fs % 4 == 0): four 16-byte vectors of Z per thread, kEwBlock apart, all loaded
-// before the first is processed; the 4 values of a vector share one bias row position.
+// before the first is processed; the 4 values of a vector share one bias row position. The
+// bias column of the first vector is one 64-bit remainder per thread; the next vectors' columns
+// are 4 kEwBlock elements further on, so each follows by one add and at most one subtraction
+// (`step` = 4 kEwBlock mod Fs, from the host).
 template <class T, int ACT>
 __global__ __launch_bounds__(kEwBlock) void bias_act_vec(const float* __restrict__ Z,
                                                          const T* __restrict__ b,
                                                          T* __restrict__ H, int64_t nvec,
-                                                         int64_t Fs, int64_t v0)
+                                                         int64_t Fs, int64_t v0, int64_t step)
 {
     const int64_t base = v0 + (int64_t)blockIdx.x * (kEwBlock * kEwVecs) + threadIdx.x;
+    int64_t col = b ? (base * 4) % Fs : 0;
     f32x4 z[kEwVecs];
 #pragma unroll
     for (int u = 0; u < kEwVecs; ++u) {
@@ -84,7 +85,11 @@ __global__ __launch_bounds__(kEwBlock) void bias_act_vec(const float* __restrict
         const int64_t v = base + u * kEwBlock;
         if (v >= nvec) continue;
         f32x4 x = z[u];
-        if (b) x += bias4_at<T>(b, (v * 4) % Fs);
+        if (b) {
+            x += bias4_at<T>(b, col);
+            col += step;
+            if (col >= Fs) col -= Fs;
+        }
         f32x4 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = act_fwd<ACT>(x[e]);
@@ -117,7 +122,8 @@ void launch_typed(const float* Z, const T* b, T* H, int64_t N, int64_t Fs, hipSt
             const int64_t groups = ceil_div(nvec, per_group) - g0;
             hipLaunchKernelGGL((bias_act_vec<T, ACT>),
                                dim3((uint32_t)(groups < max_launch ? groups : max_launch)),
-                               dim3(kEwBlock), 0, s, Z, b, H, nvec, Fs, g0 * per_group);
+                               dim3(kEwBlock), 0, s, Z, b, H, nvec, Fs, g0 * per_group,
+                               (int64_t)(4 * kEwBlock) % Fs);
         }
     } else {
         const int64_t groups = ceil_div(n, 256) < 4096 ? ceil_div(n, 256) : 4096;
