@@ -9,21 +9,26 @@
 #include "dispatch.hpp"
 #include "launch.hpp"
 
+#include <atomic>
+
 namespace mlptp {
 
 int compute_units()
 {
-    static int cus = 0;  // queried once; the first device asked for sizes every launch
-    if (cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            n > 0)
-            cus = n;
-        else
-            cus = 256;
+    // Queried once (the first device asked sizes every launch). Atomic, so host threads that
+    // launch at the same time read either 0 (and query) or the stored count.
+    static std::atomic<int> cus{0};
+    int n = cus.load(std::memory_order_relaxed);
+    if (n == 0) {
+        int dev = 0, c = 0;
+        n = (hipGetDevice(&dev) == hipSuccess &&
+             hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+             c > 0)
+                ? c
+                : 256;
+        cus.store(n, std::memory_order_relaxed);
     }
-    return cus;
+    return n;
 }
 
 // Z^(r) = X W1^(r) + b1^(r), H^(r) = phi(Z^(r)) [Z 02], [J 7.2 列并行].
