@@ -237,6 +237,11 @@ def main() -> int:
         "arch": getattr(props, "gcnArchName", None),
         "compute_units": props.multi_processor_count,
         "sclk_mhz_during_timing": sclk_mhz,
+        # value over the dense bf16 rate at the clock the driver reported during the timed steps
+        # (CUs x 4096 FLOP/clock x sclk): context for box-to-box clock spread, not the roofline.
+        "pct_of_peak_at_reported_sclk": (round(100.0 * value / (props.multi_processor_count * 4096.0
+                                                                  * sclk_mhz * 1e-6), 2)
+                                         if sclk_mhz else None),
         "hip": getattr(torch.version, "hip", None),
     }
     print(json.dumps(out), flush=True)
