@@ -32,8 +32,11 @@
  *     NULL is the null stream). The library never allocates, frees or synchronises; the
  *     caller owns all memory and must keep it alive until the stream has run the work.
  *   - Every argument is validated on the host BEFORE any HIP call; a failed check returns its
- *     negative code and launches nothing. MLP_TP_E_HIP reports a launch failure seen by
- *     hipGetLastError after the launches (the stream may then hold part of the work).
+ *     negative code and launches nothing.
+ *   - MLP_TP_E_HIP has two sources. (a) A HIP error was already pending on the calling thread
+ *     (left by earlier work) when the call was about to launch: nothing is launched and that
+ *     error stays pending for the caller's hipGetLastError. (b) One of this call's own launches
+ *     failed: the error is cleared, and the stream may hold part of the call's work.
  *   - Outputs must not overlap inputs or each other (MLP_TP_E_ALIAS), except where stated.
  */
 #ifndef MLP_TP_H
@@ -199,6 +202,23 @@ int mlp_tp_down_proj_overlap_tail(const void* H, const void* W2r, const float* c
                                   int64_t chunk_rows, void* stream, void* tail_stream);
 
 /*
+ * Row-parallel down-projection with rank r's share of b2 [Z 05]:
+ *     P = H . W2r + b2 / T        (fp32; b2[d] / T rounded once to fp32, then added)
+ * The alternative [Z 05] names to adding b2 once after the sum: every rank adds b2 / T to its
+ * own partial, so the plain sum of the T partials (mlp_tp_partial_reduce with b2 = NULL) holds
+ * b2 once. For T a power of two, b2 / T is exact and the result equals the b2-once tail on
+ * exactly representable data; for other T it differs by the rounding of b2 / T and of the
+ * extra additions (mlp_tp_partial_reduce's b2 argument is the exact form).
+ *   H [N, Fs], W2r [Fs, D]: dtype, as for mlp_tp_down_proj.
+ *   b2 [D] of b2_dtype (MLP_TP_F32 or MLP_TP_BF16), the FULL bias; NULL adds nothing.
+ *   P [N, D] float output.
+ * Errors: those of mlp_tp_down_proj, E_DTYPE (b2_dtype), E_ALIGN (b2), E_ALIAS (P over b2).
+ */
+int mlp_tp_down_proj_bias_share(const void* H, const void* W2r, const void* b2, int32_t b2_dtype,
+                                float* P, int64_t N, int64_t D, int64_t F, int32_t T,
+                                int32_t dtype, void* stream);
+
+/*
  * Gated (SwiGLU) up-projection [Z 08]: the gate and up projections are cut at the SAME columns,
  * so each rank multiplies matching channels locally:
  *     G = X . Wgr,   U = X . Wur   (fp32 accumulate),   H = SiLU(G) * U,   SiLU(z) = z sigmoid(z).
@@ -294,6 +314,29 @@ int mlp_tp_swiglu_shard_bwd(const void* X, const void* Wgr, const void* Wur, con
  */
 int mlp_tp_bias_act(const float* Z, const void* b1r, void* H, int64_t N, int64_t F, int32_t T,
                     int32_t dtype, int32_t act, void* stream);
+
+/* Products of one rank's shard, named for mlp_tp_shard_tile. */
+#define MLP_TP_PROD_UP 0   /* X . W1r       [N, Fs]  up-projection             [Z 02] */
+#define MLP_TP_PROD_DOWN 1 /* H . W2r       [N, D]   down-projection           [Z 02] */
+#define MLP_TP_PROD_DH 2   /* dY . W2r^T    [N, Fs]  backward through W2r      [Z 06] */
+#define MLP_TP_PROD_DW2 3  /* H^T . dY      [Fs, D]  weight gradient of W2r    [Z 06] */
+#define MLP_TP_PROD_DW1 4  /* X^T . dZ      [D, Fs]  weight gradient of W1r    [Z 06] */
+#define MLP_TP_PROD_DX 5   /* dZ . W1r^T    [N, D]   input-gradient partial    [Z 06] */
+
+/*
+ * The output tile a bf16 product of one rank's shard runs on, on a GPU of compute_units
+ * compute units: *tile_rows x *tile_cols results of the product per workgroup; *staged is 1
+ * when the shape takes the register-staged kernel (a leading dimension, K, or an m/n-contiguous
+ * extent not a multiple of 8) and 0 for the direct-to-LDS kernel. A host query for tuning and
+ * tests: it calls no HIP function and launches nothing.
+ *   product  one of MLP_TP_PROD_*; N, D, F, T as for the shard calls (N > 0 here).
+ *   tile_rows, tile_cols, staged  HOST pointers (each may be NULL if not wanted).
+ * Errors: E_SHAPE (sizes as for the shard calls, N == 0, or compute_units < 1),
+ * E_INDIVISIBLE, E_DTYPE (product outside the list).
+ */
+int mlp_tp_shard_tile(int32_t product, int64_t N, int64_t D, int64_t F, int32_t T,
+                      int32_t compute_units, int32_t* tile_rows, int32_t* tile_cols,
+                      int32_t* staged);
 
 /* Static description of a return code; never NULL. */
 const char* mlp_tp_strerror(int code);

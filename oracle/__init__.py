@@ -40,6 +40,7 @@ def _load():
         lib.oracle_act_deriv_vec.argtypes = [ci, vp, vp, i64]
         lib.oracle_shard_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, ci, vp, vp, vp]
         lib.oracle_partial_sum.argtypes = [vp, i32, vp, i64, i64, vp]
+        lib.oracle_partial_sum_bias_share.argtypes = [vp, i32, i32, vp, i64, i64, vp]
         lib.oracle_block_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, ci, vp]
         lib.oracle_dense_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
         lib.oracle_shard_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, ci,
@@ -56,7 +57,7 @@ def _load():
         lib.oracle_swiglu_shard_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
                                                 vp, vp, vp, vp, vp, vp]
         for name in ("oracle_act_vec", "oracle_act_deriv_vec", "oracle_shard_fwd",
-                     "oracle_partial_sum", "oracle_block_fwd", "oracle_dense_fwd",
+                     "oracle_partial_sum", "oracle_partial_sum_bias_share", "oracle_block_fwd", "oracle_dense_fwd",
                      "oracle_shard_bwd", "oracle_dense_bwd", "oracle_num_threads",
                      "oracle_token_slice", "oracle_partial_reduce_scatter", "oracle_silu_vec",
                      "oracle_swiglu_shard_fwd", "oracle_swiglu_dense_fwd",
@@ -144,6 +145,23 @@ def partial_sum(partials, b2=None):
     Y = np.empty((N, D))
     _check(_load().oracle_partial_sum(ctypes.cast(arr, ctypes.c_void_p), T, _p(b2), N, D,
                                       _p(Y)), "oracle_partial_sum")
+    return Y
+
+
+def partial_sum_bias_share(partials, b2, T):
+    """b2 split over the ranks [Z 05]: Y = ((P0 + b2/T) + (P1 + b2/T)) + ... over the given
+    [N, D] partials (all T of them for the tail, or one rank's for its contribution)."""
+    Ps = [_f64(p) for p in partials]
+    N, D = Ps[0].shape
+    for p in Ps:
+        if p.shape != (N, D):
+            raise OracleError("partials differ in shape")
+    b2 = _f64(b2)
+    arr = (ctypes.c_void_p * len(Ps))(*[p.ctypes.data for p in Ps])
+    Y = np.empty((N, D))
+    _check(_load().oracle_partial_sum_bias_share(ctypes.cast(arr, ctypes.c_void_p), len(Ps), T,
+                                                 _p(b2), N, D, _p(Y)),
+           "oracle_partial_sum_bias_share")
     return Y
 
 

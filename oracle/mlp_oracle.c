@@ -17,6 +17,7 @@
  *     H^(r) = phi(Z^(r))                     activation, local per shard     [Z 02], [C MLP 为什么先 column 后 row]
  *     P^(r) = H^(r) . W2[c, :]               row-parallel down-projection    [Z 02], [J 7.2]
  *     Y     = ((P^(0) + P^(1)) + ...) + b2   block-tail sum, b2 added once   [Z 02], [Z 05], [U 3.8]
+ *     or, b2 split over the ranks: Y = ((P^(0) + b2/T) + (P^(1) + b2/T)) + ...      [Z 05]
  *   backward of shard r for an upstream gradient dY of Y:
  *     dH^(r)  = dY . W2[c, :]^T              no exchange                     [Z 06], [U 3.6.1]
  *     dZ^(r)  = dH^(r) (.) phi'(Z^(r))       through the local activation    [Z 06]
@@ -234,6 +235,33 @@ int oracle_partial_sum(const double* const* P, int32_t T, const double* b2, int6
             double s = P[0][n * D + d];
             for (int32_t r = 1; r < T; ++r) s += P[r][n * D + d];
             if (b2) s += b2[d];
+            Y[n * D + d] = s;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Block tail with b2 split over the ranks, the alternative [Z 05] offers to adding b2 once:
+ * every rank adds b2 / T to its own partial before the exchange, and the exchange sums those:
+ *     Y = ((P^(0) + b2/T) + (P^(1) + b2/T)) + ...
+ * over the nparts partials given (nparts = T for the whole tail; nparts = 1 gives one rank's
+ * contribution P^(r) + b2/T). Each contribution is formed first, then the contributions are
+ * summed in rank order. b2 may be NULL (then this is the plain sum).
+ */
+int oracle_partial_sum_bias_share(const double* const* P, int32_t nparts, int32_t T,
+                                  const double* b2, int64_t N, int64_t D, double* Y)
+{
+    if (N <= 0 || D <= 0 || T < 1 || nparts < 1) return -2;
+    if (!P || !Y) return -1;
+    for (int32_t r = 0; r < nparts; ++r)
+        if (!P[r]) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t d = 0; d < D; ++d) {
+            const double share = b2 ? b2[d] / (double)T : 0.0;
+            double s = P[0][n * D + d] + share;
+            for (int32_t r = 1; r < nparts; ++r) s += P[r][n * D + d] + share;
             Y[n * D + d] = s;
         }
     }

@@ -25,6 +25,7 @@ E_NULL, E_SHAPE, E_INDIVISIBLE, E_DTYPE, E_ACT, E_ALIGN, E_WORKSPACE, E_HIP, E_A
 F32, BF16 = 0, 1
 ACT = {"identity": 0, "relu": 1, "gelu_tanh": 2, "gelu_erf": 3, "gelu_sigmoid": 4}
 MAX_REDUCE_T = 64
+PROD = {"up": 0, "down": 1, "dh": 2, "dw2": 3, "dw1": 4, "dx": 5}
 
 _lib = None
 
@@ -57,6 +58,9 @@ def load() -> ctypes.CDLL:
         "mlp_tp_partial_reduce_scatter": ([vp, i32, i32, vp, i32, vp, i64, i64, vp],
                                           ctypes.c_int),
         "mlp_tp_down_proj_accumulate": ([vp, vp, vp, i64, i64, i64, i32, i32, vp], ctypes.c_int),
+        "mlp_tp_down_proj_bias_share": ([vp, vp, vp, i32, vp, i64, i64, i64, i32, i32, vp],
+                                        ctypes.c_int),
+        "mlp_tp_shard_tile": ([i32, i64, i64, i64, i32, i32, vp, vp, vp], ctypes.c_int),
         "mlp_tp_down_proj_overlap_tail": ([vp, vp, vp, i32, i32, vp, i32, vp, i64, i64, i64, i32,
                                            i64, vp, vp], ctypes.c_int),
         "mlp_tp_swiglu_up_proj": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp],
@@ -87,12 +91,47 @@ def strerror(code: int) -> str:
     return load().mlp_tp_strerror(int(code)).decode()
 
 
-def _ptr(x):
+_TORCH_DTYPES = {}
+
+
+def _torch_dtype(code):
+    """torch dtype of a dtype code (F32 or BF16); None for an unknown code (the library then
+    rejects the call with E_DTYPE)."""
+    if not _TORCH_DTYPES:
+        import torch
+        _TORCH_DTYPES.update({F32: torch.float32, BF16: torch.bfloat16})
+    return _TORCH_DTYPES.get(code)
+
+
+def _ptr(x, dtype=None, name="tensor"):
+    """Device address of x: None -> NULL, an int is taken as an address, a torch tensor must be
+    contiguous (row-major, no padding: a column slice such as W1[:, c0:c1] is not), of the
+    element type `dtype` (a dtype code; None skips the check, e.g. for a byte workspace), and
+    in GPU memory. Marshalling checks only: they raise ValueError before the library is
+    called."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major, no padding); pass "
+                         f"a .contiguous() copy")
+    if dtype is not None:
+        want = _torch_dtype(dtype)
+        if want is not None and x.dtype != want:
+            raise ValueError(f"{name} has dtype {x.dtype}, the call's dtype code {dtype} "
+                             f"needs {want}")
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be in GPU memory")
     return x.data_ptr()
+
+
+def _ptr_array(P, T, name="P"):
+    """Host array of the T device pointers of the partials (float32 tensors or addresses)."""
+    if len(P) != T:
+        raise ValueError(f"{name} holds {len(P)} partials but T = {T}")
+    ptrs = [_ptr(p, F32, f"{name}[{i}]") for i, p in enumerate(P)]
+    return (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
 
 
 def _stream(stream):
@@ -115,28 +154,33 @@ def _check(rc: int, func: str) -> int:
 
 
 def mlp_tp_up_proj(X, W1r, b1r, Z, H, N, D, F, T, dtype, act, stream=None):
-    rc = load().mlp_tp_up_proj(_ptr(X), _ptr(W1r), _ptr(b1r), _ptr(Z), _ptr(H), N, D, F, T,
-                               dtype, _act(act), _stream(stream))
+    rc = load().mlp_tp_up_proj(_ptr(X, dtype, "X"), _ptr(W1r, dtype, "W1r"),
+                               _ptr(b1r, dtype, "b1r"), _ptr(Z, dtype, "Z"), _ptr(H, dtype, "H"),
+                               N, D, F, T, dtype, _act(act), _stream(stream))
     return _check(rc, "mlp_tp_up_proj")
 
 
 def mlp_tp_down_proj(H, W2r, P, N, D, F, T, dtype, stream=None):
-    rc = load().mlp_tp_down_proj(_ptr(H), _ptr(W2r), _ptr(P), N, D, F, T, dtype,
-                                 _stream(stream))
+    rc = load().mlp_tp_down_proj(_ptr(H, dtype, "H"), _ptr(W2r, dtype, "W2r"),
+                                 _ptr(P, F32, "P"), N, D, F, T, dtype, _stream(stream))
     return _check(rc, "mlp_tp_down_proj")
 
 
 def mlp_tp_shard_fwd(X, W1r, b1r, W2r, H, Z, P, N, D, F, T, dtype, act, stream=None):
-    rc = load().mlp_tp_shard_fwd(_ptr(X), _ptr(W1r), _ptr(b1r), _ptr(W2r), _ptr(H), _ptr(Z),
-                                 _ptr(P), N, D, F, T, dtype, _act(act), _stream(stream))
+    rc = load().mlp_tp_shard_fwd(_ptr(X, dtype, "X"), _ptr(W1r, dtype, "W1r"),
+                                 _ptr(b1r, dtype, "b1r"), _ptr(W2r, dtype, "W2r"),
+                                 _ptr(H, dtype, "H"), _ptr(Z, dtype, "Z"), _ptr(P, F32, "P"),
+                                 N, D, F, T, dtype, _act(act), _stream(stream))
     return _check(rc, "mlp_tp_shard_fwd")
 
 
 def mlp_tp_partial_reduce(P, T, b2, b2_dtype, Y, N, D, stream=None):
-    """P: a sequence of T device tensors/pointers (passed as a host array of pointers)."""
-    ptrs = (ctypes.c_void_p * max(1, len(P)))(*[_ptr(p) for p in P])
-    rc = load().mlp_tp_partial_reduce(ctypes.cast(ptrs, ctypes.c_void_p), T, _ptr(b2), b2_dtype,
-                                      _ptr(Y), N, D, _stream(stream))
+    """P: a sequence of exactly T float32 device tensors or addresses (passed as a host array
+    of pointers)."""
+    ptrs = _ptr_array(P, T)
+    rc = load().mlp_tp_partial_reduce(ctypes.cast(ptrs, ctypes.c_void_p), T,
+                                      _ptr(b2, b2_dtype, "b2"), b2_dtype, _ptr(Y, F32, "Y"), N, D,
+                                      _stream(stream))
     return _check(rc, "mlp_tp_partial_reduce")
 
 
@@ -151,41 +195,71 @@ def mlp_tp_token_slice(N, T, r):
 
 def mlp_tp_partial_reduce_scatter(P, T, r, b2, b2_dtype, Yr, N, D, stream=None):
     """Token slice r of the block tail into Yr [rows, D]; P as for mlp_tp_partial_reduce."""
-    ptrs = (ctypes.c_void_p * max(1, len(P)))(*[_ptr(p) for p in P])
-    rc = load().mlp_tp_partial_reduce_scatter(ctypes.cast(ptrs, ctypes.c_void_p), T, r, _ptr(b2),
-                                              b2_dtype, _ptr(Yr), N, D, _stream(stream))
+    ptrs = _ptr_array(P, T)
+    rc = load().mlp_tp_partial_reduce_scatter(ctypes.cast(ptrs, ctypes.c_void_p), T, r,
+                                              _ptr(b2, b2_dtype, "b2"), b2_dtype,
+                                              _ptr(Yr, F32, "Yr"), N, D, _stream(stream))
     return _check(rc, "mlp_tp_partial_reduce_scatter")
 
 
 def mlp_tp_down_proj_accumulate(H, W2r, P, N, D, F, T, dtype, stream=None):
-    rc = load().mlp_tp_down_proj_accumulate(_ptr(H), _ptr(W2r), _ptr(P), N, D, F, T, dtype,
+    rc = load().mlp_tp_down_proj_accumulate(_ptr(H, dtype, "H"), _ptr(W2r, dtype, "W2r"),
+                                            _ptr(P, F32, "P"), N, D, F, T, dtype,
                                             _stream(stream))
     return _check(rc, "mlp_tp_down_proj_accumulate")
+
+
+def mlp_tp_down_proj_bias_share(H, W2r, b2, b2_dtype, P, N, D, F, T, dtype, stream=None):
+    """P = H W2r + b2 / T: rank r's partial carrying its 1/T share of the full bias b2."""
+    rc = load().mlp_tp_down_proj_bias_share(_ptr(H, dtype, "H"), _ptr(W2r, dtype, "W2r"),
+                                            _ptr(b2, b2_dtype, "b2"), b2_dtype,
+                                            _ptr(P, F32, "P"), N, D, F, T, dtype,
+                                            _stream(stream))
+    return _check(rc, "mlp_tp_down_proj_bias_share")
+
+
+def mlp_tp_shard_tile(product, N, D, F, T, compute_units):
+    """(tile rows, tile cols, staged) of a bf16 product of the shard; product is a PROD key or
+    code. A host query: no GPU needed."""
+    code = PROD[product] if isinstance(product, str) else int(product)
+    rows, cols, staged = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    rc = load().mlp_tp_shard_tile(code, N, D, F, T, compute_units,
+                                  ctypes.cast(ctypes.byref(rows), ctypes.c_void_p),
+                                  ctypes.cast(ctypes.byref(cols), ctypes.c_void_p),
+                                  ctypes.cast(ctypes.byref(staged), ctypes.c_void_p))
+    _check(rc, "mlp_tp_shard_tile")
+    return rows.value, cols.value, staged.value
 
 
 def mlp_tp_down_proj_overlap_tail(H, W2r, P, T, r, b2, b2_dtype, Y, N, D, F, dtype, chunk_rows,
                                   stream=None, tail_stream=None):
     """P[r] = H W2r in token chunks on `stream`, the block tail of each finished chunk on
     `tail_stream` (default: the same stream)."""
-    ptrs = (ctypes.c_void_p * max(1, len(P)))(*[_ptr(p) for p in P])
+    ptrs = _ptr_array(P, T)
     s0 = _stream(stream)
     s1 = _stream(tail_stream) if tail_stream is not None else s0
-    rc = load().mlp_tp_down_proj_overlap_tail(_ptr(H), _ptr(W2r), ctypes.cast(ptrs, ctypes.c_void_p),
-                                              T, r, _ptr(b2), b2_dtype, _ptr(Y), N, D, F, dtype,
-                                              chunk_rows, s0, s1)
+    rc = load().mlp_tp_down_proj_overlap_tail(_ptr(H, dtype, "H"), _ptr(W2r, dtype, "W2r"),
+                                              ctypes.cast(ptrs, ctypes.c_void_p), T, r,
+                                              _ptr(b2, b2_dtype, "b2"), b2_dtype,
+                                              _ptr(Y, F32, "Y"), N, D, F, dtype, chunk_rows,
+                                              s0, s1)
     return _check(rc, "mlp_tp_down_proj_overlap_tail")
 
 
 def mlp_tp_swiglu_up_proj(X, Wgr, Wur, G, U, H, N, D, F, T, dtype, stream=None):
-    rc = load().mlp_tp_swiglu_up_proj(_ptr(X), _ptr(Wgr), _ptr(Wur), _ptr(G), _ptr(U), _ptr(H),
-                                      N, D, F, T, dtype, _stream(stream))
+    rc = load().mlp_tp_swiglu_up_proj(_ptr(X, dtype, "X"), _ptr(Wgr, dtype, "Wgr"),
+                                      _ptr(Wur, dtype, "Wur"), _ptr(G, dtype, "G"),
+                                      _ptr(U, dtype, "U"), _ptr(H, dtype, "H"), N, D, F, T,
+                                      dtype, _stream(stream))
     return _check(rc, "mlp_tp_swiglu_up_proj")
 
 
 def mlp_tp_swiglu_shard_fwd(X, Wgr, Wur, W2r, G, U, H, P, N, D, F, T, dtype, stream=None):
-    rc = load().mlp_tp_swiglu_shard_fwd(_ptr(X), _ptr(Wgr), _ptr(Wur), _ptr(W2r), _ptr(G),
-                                        _ptr(U), _ptr(H), _ptr(P), N, D, F, T, dtype,
-                                        _stream(stream))
+    rc = load().mlp_tp_swiglu_shard_fwd(_ptr(X, dtype, "X"), _ptr(Wgr, dtype, "Wgr"),
+                                        _ptr(Wur, dtype, "Wur"), _ptr(W2r, dtype, "W2r"),
+                                        _ptr(G, dtype, "G"), _ptr(U, dtype, "U"),
+                                        _ptr(H, dtype, "H"), _ptr(P, F32, "P"), N, D, F, T,
+                                        dtype, _stream(stream))
     return _check(rc, "mlp_tp_swiglu_shard_fwd")
 
 
@@ -198,25 +272,33 @@ def mlp_tp_shard_bwd_workspace_bytes(N, D, F, T) -> int:
 
 def mlp_tp_shard_bwd(X, W1r, W2r, Z, H, dY, dZ, dW1r, db1r, dW2r, dXr, workspace,
                      workspace_bytes, N, D, F, T, dtype, act, stream=None):
-    rc = load().mlp_tp_shard_bwd(_ptr(X), _ptr(W1r), _ptr(W2r), _ptr(Z), _ptr(H), _ptr(dY),
-                                 _ptr(dZ), _ptr(dW1r), _ptr(db1r), _ptr(dW2r), _ptr(dXr),
-                                 _ptr(workspace), int(workspace_bytes), N, D, F, T, dtype,
-                                 _act(act), _stream(stream))
+    rc = load().mlp_tp_shard_bwd(_ptr(X, dtype, "X"), _ptr(W1r, dtype, "W1r"),
+                                 _ptr(W2r, dtype, "W2r"), _ptr(Z, dtype, "Z"),
+                                 _ptr(H, dtype, "H"), _ptr(dY, dtype, "dY"),
+                                 _ptr(dZ, dtype, "dZ"), _ptr(dW1r, F32, "dW1r"),
+                                 _ptr(db1r, F32, "db1r"), _ptr(dW2r, F32, "dW2r"),
+                                 _ptr(dXr, F32, "dXr"), _ptr(workspace, None, "workspace"),
+                                 int(workspace_bytes), N, D, F, T, dtype, _act(act),
+                                 _stream(stream))
     return _check(rc, "mlp_tp_shard_bwd")
 
 
 def mlp_tp_swiglu_shard_bwd(X, Wgr, Wur, W2r, G, U, H, dY, dG, dU, dWgr, dWur, dW2r, dXr, N, D, F,
                             T, dtype, stream=None):
-    rc = load().mlp_tp_swiglu_shard_bwd(_ptr(X), _ptr(Wgr), _ptr(Wur), _ptr(W2r), _ptr(G), _ptr(U),
-                                        _ptr(H), _ptr(dY), _ptr(dG), _ptr(dU), _ptr(dWgr),
-                                        _ptr(dWur), _ptr(dW2r), _ptr(dXr), N, D, F, T, dtype,
-                                        _stream(stream))
+    rc = load().mlp_tp_swiglu_shard_bwd(_ptr(X, dtype, "X"), _ptr(Wgr, dtype, "Wgr"),
+                                        _ptr(Wur, dtype, "Wur"), _ptr(W2r, dtype, "W2r"),
+                                        _ptr(G, dtype, "G"), _ptr(U, dtype, "U"),
+                                        _ptr(H, dtype, "H"), _ptr(dY, dtype, "dY"),
+                                        _ptr(dG, dtype, "dG"), _ptr(dU, dtype, "dU"),
+                                        _ptr(dWgr, F32, "dWgr"), _ptr(dWur, F32, "dWur"),
+                                        _ptr(dW2r, F32, "dW2r"), _ptr(dXr, F32, "dXr"), N, D, F,
+                                        T, dtype, _stream(stream))
     return _check(rc, "mlp_tp_swiglu_shard_bwd")
 
 
 def mlp_tp_bias_act(Z, b1r, H, N, F, T, dtype, act, stream=None):
-    rc = load().mlp_tp_bias_act(_ptr(Z), _ptr(b1r), _ptr(H), N, F, T, dtype, _act(act),
-                                _stream(stream))
+    rc = load().mlp_tp_bias_act(_ptr(Z, F32, "Z"), _ptr(b1r, dtype, "b1r"), _ptr(H, dtype, "H"),
+                                N, F, T, dtype, _act(act), _stream(stream))
     return _check(rc, "mlp_tp_bias_act")
 
 

@@ -79,6 +79,17 @@ int disjoint(std::initializer_list<Span> outs, std::initializer_list<Span> ins)
     return MLP_TP_OK;
 }
 
+// HIP keeps one pending "last error" per host thread. An error already pending when a call is
+// about to launch belongs to earlier work (the caller's, or another library's): the call then
+// launches nothing and returns MLP_TP_E_HIP, and leaves that error pending for the caller to
+// read. Checked once per call, just before its first HIP call.
+int hip_clean()
+{
+    return hipPeekAtLastError() == hipSuccess ? MLP_TP_OK : MLP_TP_E_HIP;
+}
+
+// After this call's own launches (which started with no error pending): an error now came from
+// them; it is reported as MLP_TP_E_HIP and cleared, so later work is not blamed for it.
 int launch_status()
 {
     return hipGetLastError() == hipSuccess ? MLP_TP_OK : MLP_TP_E_HIP;
@@ -178,6 +189,7 @@ int mlp_tp_up_proj(const void* X, const void* W1r, const void* b1r, void* Z, voi
 {
     if (int rc = check_up(X, W1r, b1r, Z, H, N, D, F, T, dtype, act)) return rc;
     if (N == 0) return MLP_TP_OK;
+    if (int rc = hip_clean()) return rc;
     mlptp::launch_up_proj(X, W1r, b1r, Z, H, N, D, F / T, dtype, act,
                           static_cast<hipStream_t>(stream));
     return launch_status();
@@ -188,6 +200,7 @@ int mlp_tp_down_proj(const void* H, const void* W2r, float* P, int64_t N, int64_
 {
     if (int rc = check_down(H, W2r, P, N, D, F, T, dtype)) return rc;
     if (N == 0) return MLP_TP_OK;
+    if (int rc = hip_clean()) return rc;
     mlptp::launch_down_proj(H, W2r, P, N, D, F / T, dtype, static_cast<hipStream_t>(stream));
     return launch_status();
 }
@@ -208,6 +221,7 @@ int mlp_tp_shard_fwd(const void* X, const void* W1r, const void* b1r, const void
             return rc;
     }
     if (N == 0) return MLP_TP_OK;
+    if (int rc = hip_clean()) return rc;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     mlptp::launch_up_proj(X, W1r, b1r, Z, H, N, D, F / T, dtype, act, s);
     if (int rc = launch_status()) return rc;
@@ -224,6 +238,7 @@ int mlp_tp_partial_reduce(const float* const* P, int32_t T, const void* b2, int3
         if (P[r] != Y && overlap({Y, bytes}, {P[r], bytes})) return MLP_TP_E_ALIAS;
     if (b2 && overlap({Y, bytes}, {b2, D * elem_size(b2_dtype)})) return MLP_TP_E_ALIAS;
     if (N == 0) return MLP_TP_OK;
+    if (int rc = hip_clean()) return rc;
     mlptp::launch_partial_reduce(P, T, b2, b2_dtype, Y, N, D, static_cast<hipStream_t>(stream));
     return launch_status();
 }
@@ -252,10 +267,26 @@ int mlp_tp_partial_reduce_scatter(const float* const* P, int32_t T, int32_t r, c
     if (b2 && overlap({Yr, bytes}, {b2, D * elem_size(b2_dtype)})) return MLP_TP_E_ALIAS;
     // The slice's rows of every partial, reduced as a [rows, D] block tail. With D % 4 == 0 the
     // offset keeps each pointer 16-byte aligned; otherwise the reduce takes its element path.
+    if (int rc = hip_clean()) return rc;
     const float* Ps[MLP_TP_MAX_REDUCE_T];
     for (int32_t s = 0; s < T; ++s) Ps[s] = P[s] + row0 * D;
     mlptp::launch_partial_reduce(Ps, T, b2, b2_dtype, Yr, rows, D,
                                  static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int mlp_tp_down_proj_bias_share(const void* H, const void* W2r, const void* b2, int32_t b2_dtype,
+                                float* P, int64_t N, int64_t D, int64_t F, int32_t T,
+                                int32_t dtype, void* stream)
+{
+    if (int rc = check_down(H, W2r, P, N, D, F, T, dtype)) return rc;
+    if (b2 && !dtype_ok(b2_dtype)) return MLP_TP_E_DTYPE;
+    if (b2 && !aligned16(b2)) return MLP_TP_E_ALIGN;
+    if (b2 && overlap({P, N * D * 4}, {b2, D * elem_size(b2_dtype)})) return MLP_TP_E_ALIAS;
+    if (N == 0) return MLP_TP_OK;
+    if (int rc = hip_clean()) return rc;
+    mlptp::launch_down_proj_bias_share(H, W2r, b2, b2_dtype, P, N, D, F / T, T, dtype,
+                                       static_cast<hipStream_t>(stream));
     return launch_status();
 }
 
@@ -264,6 +295,7 @@ int mlp_tp_down_proj_accumulate(const void* H, const void* W2r, float* P, int64_
 {
     if (int rc = check_down(H, W2r, P, N, D, F, T, dtype)) return rc;
     if (N == 0) return MLP_TP_OK;
+    if (int rc = hip_clean()) return rc;
     mlptp::launch_down_proj_accumulate(H, W2r, P, N, D, F / T, dtype,
                                        static_cast<hipStream_t>(stream));
     return launch_status();
@@ -289,6 +321,7 @@ int mlp_tp_down_proj_overlap_tail(const void* H, const void* W2r, const float* c
     if (int rc = disjoint({{Y, bytes}}, {{H, N * Fs * es}, {W2r, Fs * D * es}})) return rc;
     if (b2 && overlap({Y, bytes}, {b2, D * elem_size(b2_dtype)})) return MLP_TP_E_ALIAS;
     if (N == 0) return MLP_TP_OK;
+    if (int rc = hip_clean()) return rc;
 
     const hipStream_t s0 = static_cast<hipStream_t>(stream);
     const hipStream_t s1 = static_cast<hipStream_t>(tail_stream);
@@ -322,6 +355,7 @@ int mlp_tp_swiglu_up_proj(const void* X, const void* Wgr, const void* Wur, void*
 {
     if (int rc = check_swiglu_up(X, Wgr, Wur, G, U, H, N, D, F, T, dtype)) return rc;
     if (N == 0) return MLP_TP_OK;
+    if (int rc = hip_clean()) return rc;
     mlptp::launch_swiglu_up(X, Wgr, Wur, G, U, H, N, D, F / T, dtype,
                             static_cast<hipStream_t>(stream));
     return launch_status();
@@ -344,6 +378,7 @@ int mlp_tp_swiglu_shard_fwd(const void* X, const void* Wgr, const void* Wur, con
             return rc;
     }
     if (N == 0) return MLP_TP_OK;
+    if (int rc = hip_clean()) return rc;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     mlptp::launch_swiglu_up(X, Wgr, Wur, G, U, H, N, D, F / T, dtype, s);
     if (int rc = launch_status()) return rc;
@@ -380,6 +415,7 @@ int mlp_tp_shard_bwd(const void* X, const void* W1r, const void* W2r, const void
                           {{X, N * D * es}, {W1r, D * Fs * es}, {W2r, Fs * D * es},
                            {Z, N * Fs * es}, {H, N * Fs * es}, {dY, N * D * es}}))
         return rc;
+    if (int rc = hip_clean()) return rc;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     // With N == 0 tokens dZ and dXr are empty, and the weight gradients are empty sums: the
     // K = 0 products and the column sum below then write zeros.
@@ -425,6 +461,7 @@ int mlp_tp_swiglu_shard_bwd(const void* X, const void* Wgr, const void* Wur, con
                            {W2r, Fs * D * es}, {G, N * Fs * es}, {U, N * Fs * es},
                            {H, N * Fs * es}, {dY, N * D * es}}))
         return rc;
+    if (int rc = hip_clean()) return rc;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     // With N == 0 tokens the weight gradients are empty sums: the K = 0 products write zeros.
     if (N > 0) {
@@ -461,8 +498,24 @@ int mlp_tp_bias_act(const float* Z, const void* b1r, void* H, int64_t N, int64_t
     const int64_t es = elem_size(dtype), Fs = F / T;
     if (int rc = disjoint({{H, N * Fs * es}}, {{Z, N * Fs * 4}, {b1r, Fs * es}})) return rc;
     if (N == 0) return MLP_TP_OK;
+    if (int rc = hip_clean()) return rc;
     mlptp::launch_bias_act(Z, b1r, H, N, Fs, dtype, act, static_cast<hipStream_t>(stream));
     return launch_status();
+}
+
+int mlp_tp_shard_tile(int32_t product, int64_t N, int64_t D, int64_t F, int32_t T,
+                      int32_t compute_units, int32_t* tile_rows, int32_t* tile_cols,
+                      int32_t* staged)
+{
+    if (product < MLP_TP_PROD_UP || product > MLP_TP_PROD_DX) return MLP_TP_E_DTYPE;
+    if (int rc = check_shard_shape(N, D, F, T)) return rc;
+    if (N == 0 || compute_units < 1) return MLP_TP_E_SHAPE;
+    int rows = 0, cols = 0, st = 0;
+    mlptp::shard_tile(product, N, D, F / T, compute_units, rows, cols, st);
+    if (tile_rows) *tile_rows = rows;
+    if (tile_cols) *tile_cols = cols;
+    if (staged) *staged = st;
+    return MLP_TP_OK;
 }
 
 const char* mlp_tp_strerror(int code)

@@ -26,6 +26,16 @@ using DmaTile128x128 = DmaTile<128, 128, 2, 2>;
 
 int compute_units();  // of the current device, queried once
 
+// Tiles of the bf16 GEMMs, as the chooser names them.
+enum TileKind : int {
+    kTile256x256 = 0,
+    kTile256x224 = 1,
+    kTile224x256 = 2,
+    kTile256x192 = 3,
+    kTile128x128 = 4,
+    kTileRegStaged = 5,  // register-staged fallback, 128 x 128 (shapes the direct kernel rejects)
+};
+
 // Estimated time of a tile shape: rounds of workgroups over the CU slots, times the tile area
 // over the tile's throughput relative to one 8-wave 256-class tile per CU. Measured (bf16, the
 // Llama-shape and GPT-2-medium-shape projections): a 128 x 128 workgroup runs at about 0.42 of a
@@ -33,10 +43,11 @@ int compute_units();  // of the current device, queried once
 // and the large tiles do not (a GPT-2-medium shard's down-projection: 553 instead of 350
 // TFLOP/s; a 256-token batch: 161 instead of 108) and loses otherwise (the Llama shard: 950
 // instead of 1210).
-inline int64_t tile_cost(int64_t M, int64_t N, int bm, int bn, int per_cu = 1, int rate_pct = 100)
+inline int64_t tile_cost(int64_t M, int64_t N, int bm, int bn, int64_t cus, int per_cu = 1,
+                         int rate_pct = 100)
 {
     const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
-    return ceil_div(tiles, (int64_t)compute_units() * per_cu) * bm * bn * 100 / rate_pct;
+    return ceil_div(tiles, cus * per_cu) * bm * bn * 100 / rate_pct;
 }
 
 // The direct-to-LDS kernel loads whole 16-byte chunks and addresses a tile with 32-bit byte
@@ -79,33 +90,40 @@ inline void run_dma(const void* A, const void* B, int64_t M, int64_t N, int64_t 
                        K, lda, ldb, epi);
 }
 
-// Every bf16 product goes through here: the direct-to-LDS kernel when the shape allows it,
-// else the register-staged kernel.
+// The tile a bf16 product of M x N outputs (contraction K, leading dimensions lda, ldb) runs
+// on over `cus` compute units: the register-staged kernel when the direct-to-LDS kernel cannot
+// take the shape, else the candidate of lowest cost, in order of preference (larger tiles
+// first, the first of the lowest cost wins); the narrower 256-class tiles only where they
+// divide the extent exactly. A pure function of its arguments (no HIP call).
+inline TileKind choose_tile(bool a_kc, bool b_kc, int64_t M, int64_t N, int64_t K, int64_t lda,
+                            int64_t ldb, int64_t cus)
+{
+    if (!dma_eligible(a_kc, b_kc, M, N, K, lda, ldb)) return kTileRegStaged;
+    constexpr int kCands = 5;
+    const int64_t cost[kCands] = {tile_cost(M, N, 256, 256, cus),
+                                  (N % 224 == 0) ? tile_cost(M, N, 256, 224, cus) : INT64_MAX,
+                                  (M % 224 == 0) ? tile_cost(M, N, 224, 256, cus) : INT64_MAX,
+                                  (N % 192 == 0) ? tile_cost(M, N, 256, 192, cus) : INT64_MAX,
+                                  tile_cost(M, N, 128, 128, cus, 2, 42)};
+    int best = 0;
+    for (int c = 1; c < kCands; ++c)
+        if (cost[c] < cost[best]) best = c;
+    return static_cast<TileKind>(best);
+}
+
+// Every bf16 product goes through here: the tile choose_tile picks for the current device.
 template <bool A_KC, bool B_KC, class Epi>
 inline void run_bf16(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int64_t lda,
                      int64_t ldb, Epi epi, hipStream_t s)
 {
-    if (dma_eligible(A_KC, B_KC, M, N, K, lda, ldb)) {
-        // Candidates in order of preference (larger tiles first); the first of the lowest cost
-        // wins. The narrower tiles only where they divide the extent exactly.
-        constexpr int kCands = 5;
-        const int64_t cost[kCands] = {tile_cost(M, N, 256, 256),
-                                      (N % 224 == 0) ? tile_cost(M, N, 256, 224) : INT64_MAX,
-                                      (M % 224 == 0) ? tile_cost(M, N, 224, 256) : INT64_MAX,
-                                      (N % 192 == 0) ? tile_cost(M, N, 256, 192) : INT64_MAX,
-                                      tile_cost(M, N, 128, 128, 2, 42)};
-        int best = 0;
-        for (int c = 1; c < kCands; ++c)
-            if (cost[c] < cost[best]) best = c;
-        switch (best) {
-        case 1: run_dma<DmaTile256x224, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
-        case 2: run_dma<DmaTile224x256, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
-        case 3: run_dma<DmaTile256x192, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
-        case 4: run_dma<DmaTile128x128, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
-        default: run_dma<DmaTile256x256, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
-        }
-    } else
-        run_mfma<DefaultTile, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s);
+    switch (choose_tile(A_KC, B_KC, M, N, K, lda, ldb, compute_units())) {
+    case kTile256x224: run_dma<DmaTile256x224, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
+    case kTile224x256: run_dma<DmaTile224x256, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
+    case kTile256x192: run_dma<DmaTile256x192, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
+    case kTile128x128: run_dma<DmaTile128x128, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
+    case kTileRegStaged: run_mfma<DefaultTile, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
+    default: run_dma<DmaTile256x256, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
+    }
 }
 
 template <bool A_KC, bool B_KC, class Epi>

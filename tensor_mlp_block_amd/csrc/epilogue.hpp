@@ -155,6 +155,53 @@ struct EpiStore {
 };
 using EpiStoreF32 = EpiStore<float>;
 
+// Row-parallel partial with this rank's share of b2 [Z 05]: C = v + b2[col] / T in fp32, the
+// alternative to adding b2 once after the sum. b2 (of type TB, the full bias) is divided by T
+// per column once, before the main loop; the division is IEEE (correctly rounded), so for T a
+// power of two the share is exact.
+template <class TB>
+struct EpiBiasShare {
+    float* C;
+    const TB* b2;  // [N] or nullptr
+    float T;
+    int64_t ldc;
+    int vec;
+    using ColData = f32x4;  // b2[col .. col+3] / T, zero past N or without a bias
+    using ElemData = NoData;
+    static constexpr bool kColData = true, kElemData = false;
+    __device__ __forceinline__ ColData col_load(int64_t col, int64_t N) const
+    {
+        const int64_t left = N - col;
+        const int n = left <= 0 ? 0 : (left < 4 ? (int)left : 4);
+        f32x4 b = {0.f, 0.f, 0.f, 0.f};
+        if (!b2 || !n) return b;
+        b = load4(b2 + col, n, true);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = b[e] / T;
+        return b;
+    }
+    __device__ __forceinline__ ElemData elem_load(int64_t, int64_t, int64_t, int64_t) const
+    {
+        return {};
+    }
+    __device__ __forceinline__ void apply(int64_t row, int64_t col, f32x4 v, ColData b, ElemData,
+                                          int64_t M, int64_t N) const
+    {
+        const int n = valid4(row, col, M, N);
+        if (!n) return;
+        v += b;
+        if (vec && n == 4)
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + row * ldc + col));
+        else
+            store4(C + row * ldc + col, v, n, vec);
+    }
+    __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 v, int64_t M,
+                                               int64_t N) const
+    {
+        apply(row, col, v, col_load(col, N), {}, M, N);
+    }
+};
+
 // fp32 accumulation C += v: a down-projection adding its partial into one running buffer,
 // the sequential one-GPU form of the block-tail sum [Z 02]. Each element is read and written
 // by the same lane, so the update needs no atomics.

@@ -66,6 +66,46 @@ void launch_down_proj(const void* H, const void* W2r, float* P, int64_t N, int64
         run_simt<true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
 }
 
+// P^(r) = H^(r) W2^(r) + b2 / T: each rank adds its 1/T share of b2 to its own partial, so the
+// plain sum of the partials carries b2 once [Z 05].
+void launch_down_proj_bias_share(const void* H, const void* W2r, const void* b2, int b2_dtype,
+                                 float* P, int64_t N, int64_t D, int64_t Fs, int T, int dtype,
+                                 hipStream_t s)
+{
+    auto run = [&](auto epi) {
+        if (dtype == kBF16)
+            run_bf16<true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
+        else
+            run_simt<true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
+    };
+    const int vec = (int)(D % 4 == 0);
+    if (b2_dtype == kBF16)
+        run(EpiBiasShare<uint16_t>{P, static_cast<const uint16_t*>(b2), (float)T, D, vec});
+    else
+        run(EpiBiasShare<float>{P, static_cast<const float*>(b2), (float)T, D, vec});
+}
+
+// The tile each product of the shard takes, from the same chooser its launcher runs
+// (run_bf16), with the GEMM views of the launchers in this file and in bwd.hip.
+void shard_tile(int product, int64_t N, int64_t D, int64_t Fs, int64_t cus, int& rows, int& cols,
+                int& staged)
+{
+    TileKind t = kTile256x256;
+    switch (product) {
+    case 0: t = choose_tile(true, false, N, Fs, D, D, Fs, cus); break;    // X . W1r
+    case 1: t = choose_tile(true, false, N, D, Fs, Fs, D, cus); break;    // H . W2r
+    case 2: t = choose_tile(true, true, N, Fs, D, D, D, cus); break;      // dY . W2r^T
+    case 3: t = choose_tile(false, false, Fs, D, N, Fs, D, cus); break;   // H^T . dY
+    case 4: t = choose_tile(false, false, D, Fs, N, D, Fs, cus); break;   // X^T . dZ
+    default: t = choose_tile(true, true, N, D, Fs, Fs, Fs, cus); break;   // dZ . W1r^T
+    }
+    static const int kRows[] = {256, 256, 224, 256, 128, 128};
+    static const int kCols[] = {256, 224, 256, 192, 128, 128};
+    rows = kRows[t];
+    cols = kCols[t];
+    staged = t == kTileRegStaged ? 1 : 0;
+}
+
 // P += H^(r) W2^(r): the shards of one GPU adding their partials into one running fp32 buffer
 // in turn, the sequential form of the block-tail sum [Z 02].
 void launch_down_proj_accumulate(const void* H, const void* W2r, float* P, int64_t N, int64_t D,

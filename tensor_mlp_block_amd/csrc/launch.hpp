@@ -21,6 +21,16 @@ void launch_up_proj(const void* X, const void* W1r, const void* b1r, void* Z, vo
 void launch_down_proj(const void* H, const void* W2r, float* P, int64_t N, int64_t D, int64_t Fs,
                       int dtype, hipStream_t s);
 
+// P = H W2r + b2 / T: rank r's partial carrying its share of b2. b2 [D] of b2_dtype, nullable.
+void launch_down_proj_bias_share(const void* H, const void* W2r, const void* b2, int b2_dtype,
+                                 float* P, int64_t N, int64_t D, int64_t Fs, int T, int dtype,
+                                 hipStream_t s);
+
+// The output tile (rows, cols) and kernel (staged = 1: register-staged) of a bf16 product of a
+// shard (product codes as MLP_TP_PROD_* in the C header) on `cus` compute units. Host only.
+void shard_tile(int product, int64_t N, int64_t D, int64_t Fs, int64_t cus, int& rows,
+                int& cols, int& staged);
+
 // P += H W2r (fp32 accumulation into an existing partial).
 void launch_down_proj_accumulate(const void* H, const void* W2r, float* P, int64_t N, int64_t D,
                                  int64_t Fs, int dtype, hipStream_t s);

@@ -295,3 +295,72 @@ def test_overlap_tail_checks(lib):
     assert _overlap(lib, [C, E], Y=E, N=0) == mt.OK                  # exact alias, no rows
     assert _overlap(lib, [C, E], N=0) == mt.OK
     del ctypes
+
+
+def test_tile_chooser_puts_edge_cases_on_their_tiles():
+    """The GPU edge tests run shapes meant to exercise a ragged edge (or two rounds) of each
+    256-class tile; the library's own chooser must send each product there on a 256-CU GPU."""
+    from tile_cases import EDGE_CASES, MI355X_CUS
+    for w, expect in EDGE_CASES:
+        for prod, tile in expect.items():
+            got = mt.mlp_tp_shard_tile(prod, w.N, w.D, w.F, w.T, MI355X_CUS)
+            assert got == (*tile, 0), (w.name, prod, got)
+
+
+def test_tile_chooser_headline_and_small_shapes():
+    # The Llama shard [Z 07 shapes]: 16 x 16 tiles of 256 x 224 up, 16 x 32 of 256 x 256 down.
+    assert mt.mlp_tp_shard_tile("up", 4096, 8192, 28672, 8, 256) == (256, 224, 0)
+    assert mt.mlp_tp_shard_tile("down", 4096, 8192, 28672, 8, 256) == (256, 256, 0)
+    # small products take the 128 x 128 tile; leading dimensions not multiples of 8 the
+    # register-staged kernel
+    assert mt.mlp_tp_shard_tile("down", 256, 4096, 11008, 1, 256) == (128, 128, 0)
+    assert mt.mlp_tp_shard_tile("up", 77, 200, 300, 3, 256) == (128, 128, 1)
+
+
+def test_shard_tile_checks(lib):
+    import ctypes
+    r = ctypes.c_int32()
+    rp = ctypes.cast(ctypes.byref(r), ctypes.c_void_p)
+    assert lib.mlp_tp_shard_tile(6, 4, 8, 16, 2, 256, rp, None, None) == mt.E_DTYPE
+    assert lib.mlp_tp_shard_tile(-1, 4, 8, 16, 2, 256, rp, None, None) == mt.E_DTYPE
+    assert lib.mlp_tp_shard_tile(0, 0, 8, 16, 2, 256, rp, None, None) == mt.E_SHAPE
+    assert lib.mlp_tp_shard_tile(0, 4, 8, 16, 2, 0, rp, None, None) == mt.E_SHAPE
+    assert lib.mlp_tp_shard_tile(0, 4, 8, 18, 4, 256, rp, None, None) == mt.E_INDIVISIBLE
+    assert lib.mlp_tp_shard_tile(0, 4, 8, 16, 2, 256, None, None, None) == mt.OK
+
+
+def test_bias_share_checks(lib):
+    """[Z 05] b2/T per rank: the down-projection's checks plus those of the bias."""
+    f = lib.mlp_tp_down_proj_bias_share
+    assert f(A, B, C, mt.F32, None, 4, 8, 16, 2, mt.BF16, S) == mt.E_NULL
+    assert f(A, B, C, mt.F32, E, 4, 8, 16, 3, mt.BF16, S) == mt.E_INDIVISIBLE
+    assert f(A, B, C, 7, E, 4, 8, 16, 2, mt.BF16, S) == mt.E_DTYPE
+    assert f(A, B, C + 4, mt.F32, E, 4, 8, 16, 2, mt.BF16, S) == mt.E_ALIGN
+    assert f(A, B, E, mt.F32, E, 4, 8, 16, 2, mt.BF16, S) == mt.E_ALIAS     # P over b2
+    assert f(A, B, C, mt.F32, A, 4, 8, 16, 2, mt.BF16, S) == mt.E_ALIAS     # P over H
+    assert f(A, B, C, mt.F32, E, 0, 8, 16, 2, mt.BF16, S) == mt.OK          # no tokens
+    assert f(A, B, None, 7, E, 0, 8, 16, 2, mt.BF16, S) == mt.OK            # no bias: dtype unused
+
+
+def test_binding_rejects_tensors_the_library_cannot_read():
+    """Marshalling checks of the binding, before the library is called: a column slice
+    W1[:, c0:c1] is not contiguous (read with the shard's own row stride it would give wrong
+    results), a tensor of another element type than the call's dtype code, a tensor in host
+    memory, and a partial list whose length is not T."""
+    import torch
+    W1 = torch.zeros((8, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="contiguous"):
+        mt.mlp_tp_up_proj(A, W1[:, 0:8], None, None, Dp, 4, 8, 16, 2, mt.BF16, "relu")
+    with pytest.raises(ValueError, match="dtype"):
+        mt.mlp_tp_up_proj(A, W1.float(), None, None, Dp, 4, 8, 16, 1, mt.BF16, "relu")
+    with pytest.raises(ValueError, match="GPU"):
+        mt.mlp_tp_up_proj(A, W1, None, None, Dp, 4, 8, 16, 1, mt.BF16, "relu")
+    with pytest.raises(ValueError, match="dtype"):
+        mt.mlp_tp_down_proj(A, B, torch.zeros((4, 8), dtype=torch.bfloat16), 4, 8, 16, 2, mt.BF16)
+    with pytest.raises(ValueError, match="T = 3"):
+        mt.mlp_tp_partial_reduce([A, B], 3, None, mt.F32, G, 4, 8)
+    with pytest.raises(ValueError, match="T = 1"):
+        mt.mlp_tp_partial_reduce_scatter([A, B], 1, 0, None, mt.F32, G, 4, 8)
+    with pytest.raises(ValueError, match="T = 4"):
+        mt.mlp_tp_down_proj_overlap_tail(A, B, [C, E], 4, 1, None, mt.F32, G, 4, 8, 16, mt.BF16,
+                                         2, stream=0)

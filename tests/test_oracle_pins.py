@@ -260,6 +260,53 @@ def test_b2_added_exactly_once_and_mutation_is_caught():
     assert not np.array_equal(mutant - raw, np.broadcast_to(b2, Y.shape))
 
 
+def test_bias_share_worked_example():
+    """[Z 05], the alternative to adding b2 once: every rank adds b2/T to its own partial.
+    On the worked example [Z 03] with b2 = [1,-1] (the derived variant above), rank 0
+    contributes [1,2] + [0.5,-0.5] = [1.5,1.5], rank 1 [3,3] + [0.5,-0.5] = [3.5,2.5] (by
+    hand), and the sum is [5,4], the b2-once result."""
+    g = _golden("worked_example_fwd.json")
+    parts = [np.array(p, float) for p in g["partial_per_rank"]]
+    b2 = np.array([1.0, -1.0])
+    assert np.array_equal(oracle.partial_sum_bias_share(parts[:1], b2, 2), [[1.5, 1.5]])
+    assert np.array_equal(oracle.partial_sum_bias_share(parts[1:], b2, 2), [[3.5, 2.5]])
+    assert np.array_equal(oracle.partial_sum_bias_share(parts, b2, 2), [[5.0, 4.0]])
+    assert np.array_equal(oracle.partial_sum_bias_share(parts, None, 2),
+                          np.array(g["Y_sharded"], float))
+
+
+@pytest.mark.parametrize("T", (1, 2, 4, 8))
+def test_bias_share_equals_b2_once_for_power_of_two_T(T):
+    """[Z 05]: with b2/T on every rank the tail holds b2 exactly once. On integer data and T a
+    power of two, b2/T is a short binary fraction, so the result equals the b2-once block
+    exactly; forgetting the division (Y + (T-1) b2) or adding the share on one rank only
+    (Y - (T-1) b2/T) would not."""
+    X, W1, b1, W2, b2 = _int_case(16, 16, 64, seed=16)
+    assert np.any(b2 != 0)
+    partials = [oracle.shard_fwd(X, W1, b1, W2, T, r, act="relu")[2] for r in range(T)]
+    once = oracle.block_fwd(X, W1, b1, W2, b2, T, act="relu")
+    share = oracle.partial_sum_bias_share(partials, b2, T)
+    assert np.array_equal(share, once)
+    assert np.array_equal(share - oracle.partial_sum(partials), np.broadcast_to(b2, share.shape))
+    # one rank's contribution carries exactly a 1/T share
+    c0 = oracle.partial_sum_bias_share(partials[:1], b2, T)
+    assert np.array_equal((c0 - partials[0]) * T, np.broadcast_to(b2, c0.shape))
+
+
+@pytest.mark.parametrize("T", (3, 6))
+def test_bias_share_at_other_T_differs_only_by_rounding(T):
+    """For T not a power of two b2/T is inexact; the tail then differs from the b2-once block by
+    rounding only (a few fp64 ulps of the largest value), far below the per-rank mistake."""
+    X, W1, b1, W2, b2 = _int_case(16, 16, 96, seed=17)
+    partials = [oracle.shard_fwd(X, W1, b1, W2, T, r, act="relu")[2] for r in range(T)]
+    once = oracle.block_fwd(X, W1, b1, W2, b2, T, act="relu")
+    share = oracle.partial_sum_bias_share(partials, b2, T)
+    bound = 4 * T * np.finfo(float).eps * np.max(np.abs(once))
+    assert np.max(np.abs(share - once)) <= bound
+    mutant = oracle.partial_sum([p + b2 for p in partials])
+    assert np.max(np.abs(mutant - once)) > 1e6 * bound
+
+
 def test_b1_shards_concatenate_to_unsharded_preactivation():
     """[Z 05]: the up-projection bias splits with W1's columns, so concatenating every
     shard's Z gives X W1 + b1 (numpy), exactly on integer data."""

@@ -465,8 +465,10 @@ def test_zero_tokens_leave_outputs_untouched_and_zero_weight_grads():
     """N = 0 tokens: the forward is a no-op and the weight gradients are empty sums (zeros)."""
     W1 = torch.randn((64, 64), device="cuda").bfloat16()
     W2 = torch.randn((64, 64), device="cuda").bfloat16()
-    # Zero-row activations still need valid aligned pointers: use small placeholders.
-    d = [torch.full((16,), 3.0, device="cuda") for _ in range(8)]
+    # Zero-row activations still need valid aligned pointers: small placeholders of each
+    # argument's element type (P and dXr are float, the rest bf16).
+    d = [torch.full((16,), 3.0, device="cuda",
+                    dtype=torch.float32 if i in (3, 6) else torch.bfloat16) for i in range(8)]
     mt.mlp_tp_shard_fwd(d[0], W1, None, W2, d[1], d[2], d[3], 0, 64, 128, 2, mt.BF16,
                         "gelu_tanh")
     dW1 = torch.full((64, 64), 7.0, device="cuda")

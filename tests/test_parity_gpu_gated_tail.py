@@ -155,7 +155,8 @@ def test_gated_zero_tokens_is_a_no_op():
     Wg = torch.randn((64, 64), device="cuda").bfloat16()
     Wu = torch.randn((64, 64), device="cuda").bfloat16()
     W2 = torch.randn((64, 64), device="cuda").bfloat16()
-    d = [torch.full((16,), 3.0, device="cuda") for _ in range(5)]
+    d = [torch.full((16,), 3.0, device="cuda",
+                    dtype=torch.float32 if i == 4 else torch.bfloat16) for i in range(5)]
     mt.mlp_tp_swiglu_shard_fwd(d[0], Wg, Wu, W2, d[1], d[2], d[3], d[4], 0, 64, 128, 2, mt.BF16)
     torch.cuda.synchronize()
     for t in d:
@@ -228,7 +229,8 @@ def test_gated_backward_zero_tokens_zeroes_weight_gradients():
     Wg = torch.randn((D, Fs), device="cuda").bfloat16()
     Wu = torch.randn((D, Fs), device="cuda").bfloat16()
     W2 = torch.randn((Fs, D), device="cuda").bfloat16()
-    d = [torch.full((16,), 3.0, device="cuda") for _ in range(8)]
+    d = [torch.full((16,), 3.0, device="cuda",
+                    dtype=torch.float32 if i == 7 else torch.bfloat16) for i in range(8)]
     dWg = torch.full((D, Fs), 5.0, device="cuda")
     dWu = torch.full((D, Fs), 5.0, device="cuda")
     dW2 = torch.full((Fs, D), 5.0, device="cuda")

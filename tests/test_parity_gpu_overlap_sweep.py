@@ -80,7 +80,9 @@ def _shard(w, X, r):
 OVERLAP = [
     # exact integer data: the overlapped tail must equal the oracle bit for bit
     (workloads.INT_EXACT, 16),
-    # bf16, ragged token count: the last chunk is short, the 256x224 / 256x256 tiles ragged
+    # bf16, ragged token count: the last chunk is short; these small products run on the
+    # 128 x 128 tile with ragged edges (the 256-class tiles' edges are covered by
+    # test_parity_gpu_tiles.py)
     (Workload("overlap_n300_d520_f1552_t2", 300, 520, 1552, 2, "gelu_tanh", "bf16", 8201,
               "normal"), 128),
     (Workload("overlap_n515_d264_f1024_t4", 515, 264, 1024, 4, "relu", "bf16", 8202, "normal"),
