@@ -279,6 +279,25 @@ int mlp_tp_shard_bwd(const void* X, const void* W1r, const void* W2r, const void
                      void* stream);
 
 /*
+ * mlp_tp_shard_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same computation and
+ * results, with the column-sum workspace taken from a library-owned device buffer of
+ * MLP_TP_NOALLOC_SCRATCH_BYTES per GPU (a static device array, resident until the process
+ * ends) instead of an argument. The call allocates nothing.
+ *   Arguments and outputs as mlp_tp_shard_bwd, without workspace and workspace_bytes.
+ *   Every call on one GPU shares that GPU's buffer: calls that can overlap on one GPU (other
+ *   streams, other host threads) race on it and must be ordered by the caller.
+ * Errors: those of mlp_tp_shard_bwd, and E_WORKSPACE when db1r is requested and
+ * mlp_tp_shard_bwd_workspace_bytes(N, D, F, T) exceeds MLP_TP_NOALLOC_SCRATCH_BYTES;
+ * E_HIP also when the buffer's device address cannot be obtained.
+ */
+#define MLP_TP_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+int mlp_tp_shard_bwd_noalloc(const void* X, const void* W1r, const void* W2r, const void* Z,
+                             const void* H, const void* dY, void* dZ, float* dW1r, float* db1r,
+                             float* dW2r, float* dXr, int64_t N, int64_t D, int64_t F, int32_t T,
+                             int32_t dtype, int32_t act, void* stream);
+
+/*
  * Backward of one rank's gated (SwiGLU) shard [Z 08] for the upstream gradient dY, by the
  * same rules as mlp_tp_shard_bwd [Z 06], [U 3.6.1] with the product rule through
  * H = SiLU(G) * U:

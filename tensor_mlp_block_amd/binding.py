@@ -25,6 +25,7 @@ E_NULL, E_SHAPE, E_INDIVISIBLE, E_DTYPE, E_ACT, E_ALIGN, E_WORKSPACE, E_HIP, E_A
 F32, BF16 = 0, 1
 ACT = {"identity": 0, "relu": 1, "gelu_tanh": 2, "gelu_erf": 3, "gelu_sigmoid": 4}
 MAX_REDUCE_T = 64
+NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024
 PROD = {"up": 0, "down": 1, "dh": 2, "dw2": 3, "dw1": 4, "dx": 5}
 
 _lib = None
@@ -67,6 +68,8 @@ def load() -> ctypes.CDLL:
                                   ctypes.c_int),
         "mlp_tp_swiglu_shard_fwd": ([vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
                                      vp], ctypes.c_int),
+        "mlp_tp_shard_bwd_noalloc": ([vp] * 11 + [i64, i64, i64, i32, i32, i32, vp],
+                                     ctypes.c_int),
         "mlp_tp_swiglu_shard_bwd": ([vp] * 14 + [i64, i64, i64, i32, i32, vp], ctypes.c_int),
         "mlp_tp_bias_act": ([vp, vp, vp, i64, i64, i32, i32, i32, vp], ctypes.c_int),
         "mlp_tp_strerror": ([ctypes.c_int], ctypes.c_char_p),
@@ -281,6 +284,20 @@ def mlp_tp_shard_bwd(X, W1r, W2r, Z, H, dY, dZ, dW1r, db1r, dW2r, dXr, workspace
                                  int(workspace_bytes), N, D, F, T, dtype, _act(act),
                                  _stream(stream))
     return _check(rc, "mlp_tp_shard_bwd")
+
+
+def mlp_tp_shard_bwd_noalloc(X, W1r, W2r, Z, H, dY, dZ, dW1r, db1r, dW2r, dXr, N, D, F, T,
+                             dtype, act, stream=None):
+    """mlp_tp_shard_bwd with the library's own per-GPU device buffer as the workspace (for
+    callers that cannot allocate; calls that overlap on one GPU race on that buffer)."""
+    rc = load().mlp_tp_shard_bwd_noalloc(_ptr(X, dtype, "X"), _ptr(W1r, dtype, "W1r"),
+                                         _ptr(W2r, dtype, "W2r"), _ptr(Z, dtype, "Z"),
+                                         _ptr(H, dtype, "H"), _ptr(dY, dtype, "dY"),
+                                         _ptr(dZ, dtype, "dZ"), _ptr(dW1r, F32, "dW1r"),
+                                         _ptr(db1r, F32, "db1r"), _ptr(dW2r, F32, "dW2r"),
+                                         _ptr(dXr, F32, "dXr"), N, D, F, T, dtype, _act(act),
+                                         _stream(stream))
+    return _check(rc, "mlp_tp_shard_bwd_noalloc")
 
 
 def mlp_tp_swiglu_shard_bwd(X, Wgr, Wur, W2r, G, U, H, dY, dG, dU, dWgr, dWur, dW2r, dXr, N, D, F,

@@ -393,30 +393,38 @@ int64_t mlp_tp_shard_bwd_workspace_bytes(int64_t N, int64_t D, int64_t F, int32_
     return mlptp::colsum_workspace_bytes(N, F / T);
 }
 
-int mlp_tp_shard_bwd(const void* X, const void* W1r, const void* W2r, const void* Z,
-                     const void* H, const void* dY, void* dZ, float* dW1r, float* db1r,
-                     float* dW2r, float* dXr, void* workspace, size_t workspace_bytes,
-                     int64_t N, int64_t D, int64_t F, int32_t T, int32_t dtype, int32_t act,
-                     void* stream)
+}  // extern "C"
+
+namespace {
+
+// The backward's checks except those of the workspace; *ws_need receives the bytes of
+// workspace the column sum needs (0 without db1r or without tokens).
+int check_bwd(const void* X, const void* W1r, const void* W2r, const void* Z, const void* H,
+              const void* dY, const void* dZ, const float* dW1r, const float* db1r,
+              const float* dW2r, const float* dXr, int64_t N, int64_t D, int64_t F, int32_t T,
+              int32_t dtype, int32_t act, int64_t* ws_need)
 {
     if (!X || !W1r || !W2r || !Z || !H || !dY || !dZ || !dW1r || !dW2r || !dXr)
         return MLP_TP_E_NULL;
     if (int rc = check_shard_shape(N, D, F, T)) return rc;
     if (!dtype_ok(dtype)) return MLP_TP_E_DTYPE;
     if (!act_ok(act)) return MLP_TP_E_ACT;
-    if (int rc = all_aligned({X, W1r, W2r, Z, H, dY, dZ, dW1r, db1r, dW2r, dXr, workspace}))
-        return rc;
+    if (int rc = all_aligned({X, W1r, W2r, Z, H, dY, dZ, dW1r, db1r, dW2r, dXr})) return rc;
     const int64_t es = elem_size(dtype), Fs = F / T;
-    const int64_t ws_need = (db1r && N > 0) ? mlptp::colsum_workspace_bytes(N, Fs) : 0;
-    if (ws_need > 0 && (!workspace || (int64_t)workspace_bytes < ws_need))
-        return MLP_TP_E_WORKSPACE;
-    if (int rc = disjoint({{dZ, N * Fs * es}, {dW1r, D * Fs * 4}, {db1r, Fs * 4},
-                           {dW2r, Fs * D * 4}, {dXr, N * D * 4}, {workspace, ws_need}},
-                          {{X, N * D * es}, {W1r, D * Fs * es}, {W2r, Fs * D * es},
-                           {Z, N * Fs * es}, {H, N * Fs * es}, {dY, N * D * es}}))
-        return rc;
-    if (int rc = hip_clean()) return rc;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
+    *ws_need = (db1r && N > 0) ? mlptp::colsum_workspace_bytes(N, Fs) : 0;
+    return disjoint({{dZ, N * Fs * es}, {dW1r, D * Fs * 4}, {db1r, Fs * 4}, {dW2r, Fs * D * 4},
+                     {dXr, N * D * 4}},
+                    {{X, N * D * es}, {W1r, D * Fs * es}, {W2r, Fs * D * es}, {Z, N * Fs * es},
+                     {H, N * Fs * es}, {dY, N * D * es}});
+}
+
+// The backward's launches on stream s [Z 06], [U 3.6.1]; `workspace` holds the column sum's
+// workspace (every byte the column sum reads it writes first, so nothing needs clearing).
+int run_bwd(const void* X, const void* W1r, const void* W2r, const void* Z, const void* H,
+            const void* dY, void* dZ, float* dW1r, float* db1r, float* dW2r, float* dXr,
+            void* workspace, int64_t N, int64_t D, int64_t Fs, int32_t dtype, int32_t act,
+            hipStream_t s)
+{
     // With N == 0 tokens dZ and dXr are empty, and the weight gradients are empty sums: the
     // K = 0 products and the column sum below then write zeros.
     if (N > 0) {
@@ -439,6 +447,58 @@ int mlp_tp_shard_bwd(const void* X, const void* W1r, const void* W2r, const void
         mlptp::launch_dx(dZ, W1r, dXr, N, D, Fs, dtype, s);
     }
     return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mlp_tp_shard_bwd(const void* X, const void* W1r, const void* W2r, const void* Z,
+                     const void* H, const void* dY, void* dZ, float* dW1r, float* db1r,
+                     float* dW2r, float* dXr, void* workspace, size_t workspace_bytes,
+                     int64_t N, int64_t D, int64_t F, int32_t T, int32_t dtype, int32_t act,
+                     void* stream)
+{
+    int64_t ws_need = 0;
+    if (int rc = check_bwd(X, W1r, W2r, Z, H, dY, dZ, dW1r, db1r, dW2r, dXr, N, D, F, T, dtype,
+                           act, &ws_need))
+        return rc;
+    if (workspace && !aligned16(workspace)) return MLP_TP_E_ALIGN;
+    if (ws_need > 0 && (!workspace || (int64_t)workspace_bytes < ws_need))
+        return MLP_TP_E_WORKSPACE;
+    {
+        const int64_t es = elem_size(dtype), Fs = F / T;
+        if (int rc = disjoint({{workspace, ws_need}},
+                              {{dZ, N * Fs * es}, {dW1r, D * Fs * 4}, {db1r, Fs * 4},
+                               {dW2r, Fs * D * 4}, {dXr, N * D * 4}, {X, N * D * es},
+                               {W1r, D * Fs * es}, {W2r, Fs * D * es}, {Z, N * Fs * es},
+                               {H, N * Fs * es}, {dY, N * D * es}}))
+            return rc;
+    }
+    if (int rc = hip_clean()) return rc;
+    return run_bwd(X, W1r, W2r, Z, H, dY, dZ, dW1r, db1r, dW2r, dXr, workspace, N, D, F / T,
+                   dtype, act, static_cast<hipStream_t>(stream));
+}
+
+int mlp_tp_shard_bwd_noalloc(const void* X, const void* W1r, const void* W2r, const void* Z,
+                             const void* H, const void* dY, void* dZ, float* dW1r, float* db1r,
+                             float* dW2r, float* dXr, int64_t N, int64_t D, int64_t F, int32_t T,
+                             int32_t dtype, int32_t act, void* stream)
+{
+    static_assert(MLP_TP_NOALLOC_SCRATCH_BYTES == mlptp::kNoallocScratchBytes,
+                  "the header states the buffer's size");
+    int64_t ws_need = 0;
+    if (int rc = check_bwd(X, W1r, W2r, Z, H, dY, dZ, dW1r, db1r, dW2r, dXr, N, D, F, T, dtype,
+                           act, &ws_need))
+        return rc;
+    if (ws_need > MLP_TP_NOALLOC_SCRATCH_BYTES) return MLP_TP_E_WORKSPACE;
+    if (int rc = hip_clean()) return rc;
+    // The library's own device buffer of the current GPU stands in for the workspace argument;
+    // only its address (looked up once per device) is used, nothing is allocated.
+    void* scratch = nullptr;
+    if (ws_need > 0 && mlptp::noalloc_scratch(&scratch) != 0) return MLP_TP_E_HIP;
+    return run_bwd(X, W1r, W2r, Z, H, dY, dZ, dW1r, db1r, dW2r, dXr, scratch, N, D, F / T, dtype,
+                   act, static_cast<hipStream_t>(stream));
 }
 
 int mlp_tp_swiglu_shard_bwd(const void* X, const void* Wgr, const void* Wur, const void* W2r,

@@ -7,7 +7,33 @@
 #include "dispatch.hpp"
 #include "launch.hpp"
 
+#include <mutex>
+
 namespace mlptp {
+
+// Device buffer of the allocation-free backward: the db1 column sum's workspace, for callers
+// that cannot allocate (HIP graph capture, serving loops). One copy per GPU, resident until
+// the process ends. In host code `scratch` names a host-side stand-in, not a device address:
+// kernels and copies get the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+int noalloc_scratch(void** ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        // The device is current here, so this is that GPU's copy of the array.
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return -1;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return 0;
+}
 
 // dH = dY W2^(r)^T (no exchange in the row-parallel backward), then dZ = dH * phi'(Z)
 // [Z 06], [U 3.6.1]. GEMM view: M = N tokens, N = Fs, K = D; A = dY (k-contiguous),

@@ -62,6 +62,13 @@ void launch_dx(const void* dZ, const void* W1r, float* dX, int64_t N, int64_t D,
 void launch_dx_accumulate(const void* dZ, const void* W1r, float* dX, int64_t N, int64_t D,
                           int64_t Fs, int dtype, hipStream_t s);
 
+// Size of the library-owned device buffer of the allocation-free backward (per GPU).
+constexpr int64_t kNoallocScratchBytes = int64_t(8) << 20;
+
+// Device address of that buffer on the current device in *ptr (looked up once per device);
+// 0, or -1 when HIP cannot provide it. Nothing is allocated.
+int noalloc_scratch(void** ptr);
+
 // db1 [Fs] = column sums of dZ [N, Fs], deterministic two-pass through `ws`.
 int64_t colsum_workspace_bytes(int64_t N, int64_t Fs);
 void launch_colsum(const void* dZ, float* ws, float* db1, int64_t N, int64_t Fs, int dtype,

@@ -364,3 +364,29 @@ def test_binding_rejects_tensors_the_library_cannot_read():
     with pytest.raises(ValueError, match="T = 4"):
         mt.mlp_tp_down_proj_overlap_tail(A, B, [C, E], 4, 1, None, mt.F32, G, 4, 8, 16, mt.BF16,
                                          2, stream=0)
+
+
+def test_noalloc_backward_checks(lib):
+    """The allocation-free backward takes the backward's checks, and rejects on the host,
+    before any HIP call, sizes whose column-sum workspace exceeds its buffer."""
+    f = lib.mlp_tp_shard_bwd_noalloc
+
+    def call(**kw):
+        a = dict(X=A, W1r=A + 0x1000, W2r=A + 0x2000, Z=A + 0x3000, H=A + 0x4000,
+                 dY=A + 0x5000, dZ=B, dW1r=C, db1r=Dp, dW2r=E, dXr=G, N=4, D=8, F=16, T=2,
+                 dtype=mt.BF16, act=mt.ACT["gelu_tanh"])
+        a.update(kw)
+        return f(a["X"], a["W1r"], a["W2r"], a["Z"], a["H"], a["dY"], a["dZ"], a["dW1r"],
+                 a["db1r"], a["dW2r"], a["dXr"], a["N"], a["D"], a["F"], a["T"], a["dtype"],
+                 a["act"], S)
+
+    assert call(dY=None) == mt.E_NULL
+    assert call(T=3) == mt.E_INDIVISIBLE
+    assert call(act=9) == mt.E_ACT
+    assert call(dZ=A + 0x3000) == mt.E_ALIAS
+    # 32776 tokens of Fs = 4096: 513 slabs x 4096 x 4 bytes > 8 MiB
+    big = dict(X=A, W1r=B, W2r=B + (1 << 22), Z=C, H=C + (1 << 27), dY=Dp, dZ=E,
+               dW1r=G, db1r=G + (1 << 22), dW2r=G + (1 << 23), dXr=G + (1 << 24),
+               N=32776, D=64, F=4096, T=1)
+    assert mt.mlp_tp_shard_bwd_workspace_bytes(32776, 64, 4096, 1) > mt.NOALLOC_SCRATCH_BYTES
+    assert call(**big) == mt.E_WORKSPACE
