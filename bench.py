@@ -38,7 +38,7 @@ ROW_WARMUP_MS = 150.0  # each extra row, after its own input set-up
 
 ROWS = ("fwd_cold_operands", "partial_reduce", "shard_bwd", "sum_dx", "gated_shard_fwd",
         "gated_shard_bwd", "gpt3_layer", "reduce_scatter_slice", "shard_count_sweep",
-        "gpt2_medium_block", "epilogue_fusion_ablation")
+        "gpt2_medium_block", "epilogue_fusion_ablation", "small_products")
 
 
 def log(msg: str) -> None:
@@ -493,7 +493,45 @@ def measure_next_rows(torch, mt, synth, workloads, dev, g, want=ROWS):
         res.update(_row_t_sweep(torch, mt, workloads, dev, g))
     if "gpt2_medium_block" in want:
         res.update(_row_gpt2_medium(torch, mt, workloads, dev, g))
+    if "small_products" in want:
+        res.update(_row_small_products(torch, mt, workloads, dev, g))
     return res
+
+
+def _row_small_products(torch, mt, workloads, dev, g):
+    """Shards whose products have too few output tiles to fill the GPU: the pages' example shape
+    (256 tokens, D 4096, F 11008) at T = 1, 2, 4, 8 and one GPT-2-medium shard (4096 tokens, D
+    1024, F 4096, T 2), each as mlp_tp_shard_fwd and as mlp_tp_shard_fwd_ws with the workspace
+    its query asks for (products with at most half the 128 x 128 workgroup slots filled split
+    their contraction)."""
+    cases = [(workloads.PAGE_EXAMPLE_MLP.with_(T=T), f"page_example_t{T}") for T in (1, 2, 4, 8)]
+    cases.append((workloads.GPT2_MEDIUM_T2, "gpt2_medium_shard"))
+    out = {}
+    for w, key in cases:
+        N, D, F, T, Fs = w.N, w.D, w.F, w.T, w.Fs
+        X = _randn_bf16(torch, (N, D), 1.0, g, dev)
+        W1 = _randn_bf16(torch, (D, Fs), 0.02, g, dev)
+        b1 = _randn_bf16(torch, (Fs,), 0.02, g, dev)
+        W2 = _randn_bf16(torch, (Fs, D), 0.02, g, dev)
+        H = torch.empty((N, Fs), dtype=torch.bfloat16, device=dev)
+        P = torch.empty((N, D), device=dev)
+        nb = mt.mlp_tp_shard_fwd_workspace_bytes(N, D, F, T)
+        ws = torch.empty((max(nb, 16),), dtype=torch.uint8, device=dev)
+        plain = _time_loop(torch, lambda: mt.mlp_tp_shard_fwd(X, W1, b1, W2, H, None, P, N, D, F,
+                                                              T, mt.BF16, w.act), 50)
+        split = _time_loop(torch, lambda: mt.mlp_tp_shard_fwd_ws(X, W1, b1, W2, H, None, P, ws, nb,
+                                                                 N, D, F, T, mt.BF16, w.act), 50)
+        flop = 4.0 * N * D * Fs
+        tiles = {p: mt.mlp_tp_shard_tile(p, N, D, F, T, torch.cuda.get_device_properties(dev)
+                                         .multi_processor_count)[:2] for p in ("up", "down")}
+        out[key] = {"N": N, "D": D, "F": F, "T": T, "tiles": tiles, "workspace_bytes": nb,
+                    "ms": round(plain, 5), "TFLOP/s": round(flop / (plain * 1e-3) / 1e12, 1),
+                    "split_ms": round(split, 5),
+                    "split_TFLOP/s": round(flop / (split * 1e-3) / 1e12, 1)}
+        log(f"[bench] small products {key}: {plain:.4f} ms unsplit, {split:.4f} ms with "
+            f"{nb / 1e6:.1f} MB of workspace")
+        del X, W1, b1, W2, H, P, ws
+    return {"small_products": out}
 
 
 def _row_gpt2_medium(torch, mt, workloads, dev, g):

@@ -119,6 +119,35 @@ int mlp_tp_shard_fwd(const void* X, const void* W1r, const void* b1r, const void
                      int32_t dtype, int32_t act, void* stream);
 
 /*
+ * Bytes of device workspace mlp_tp_shard_fwd_ws uses for these sizes on the current device:
+ * 0 when both products of the shard fill the GPU unsplit. Only bf16 products split (for
+ * MLP_TP_F32 any workspace is unused). A negative MLP_TP_E_* code for invalid sizes.
+ */
+int64_t mlp_tp_shard_fwd_workspace_bytes(int64_t N, int64_t D, int64_t F, int32_t T);
+
+/*
+ * mlp_tp_shard_fwd for shards whose products have too few output tiles to fill the GPU (few
+ * tokens, or a narrow Fs or D [Z 04]): given a workspace, such a product splits its contraction
+ * over several workgroups per output tile. Each split writes an fp32 partial of the product into
+ * the workspace, and one streaming pass sums the partials in a fixed order and applies the
+ * product's own epilogue (bias and phi for the up-projection, the fp32 partial P for the
+ * down-projection). Deterministic, no atomics; the results differ from mlp_tp_shard_fwd's only
+ * in the order of the fp32 additions (both are within the same tolerance of the exact result).
+ *   Arguments as mlp_tp_shard_fwd, plus:
+ *   workspace        device scratch owned by the caller, contents not preserved; NULL with
+ *                    workspace_bytes = 0 gives exactly mlp_tp_shard_fwd.
+ *   workspace_bytes  its size. The products split only when it is at least
+ *                    mlp_tp_shard_fwd_workspace_bytes(N, D, F, T); a smaller workspace leaves
+ *                    both unsplit (the call is then exactly mlp_tp_shard_fwd).
+ * Errors: those of mlp_tp_shard_fwd, E_ALIGN (workspace), E_ALIAS (workspace overlapping any
+ * input or output).
+ */
+int mlp_tp_shard_fwd_ws(const void* X, const void* W1r, const void* b1r, const void* W2r, void* H,
+                        void* Z, float* P, void* workspace, size_t workspace_bytes, int64_t N,
+                        int64_t D, int64_t F, int32_t T, int32_t dtype, int32_t act,
+                        void* stream);
+
+/*
  * Block-tail reduction on one GPU [Z 02], [Z 04], [Z 05], [U 3.8]:
  *     Y = (((P[0] + P[1]) + ...) + P[T-1]) + b2     (fp32, shards summed in rank order,
  *                                                    b2 added exactly once, last).

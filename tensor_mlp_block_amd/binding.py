@@ -51,6 +51,9 @@ def load() -> ctypes.CDLL:
         "mlp_tp_down_proj": ([vp, vp, vp, i64, i64, i64, i32, i32, vp], ctypes.c_int),
         "mlp_tp_shard_fwd": ([vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp],
                              ctypes.c_int),
+        "mlp_tp_shard_fwd_workspace_bytes": ([i64, i64, i64, i32], ctypes.c_int64),
+        "mlp_tp_shard_fwd_ws": ([vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i32, i32, i32,
+                                 vp], ctypes.c_int),
         "mlp_tp_partial_reduce": ([vp, i32, vp, i32, vp, i64, i64, vp], ctypes.c_int),
         "mlp_tp_shard_bwd_workspace_bytes": ([i64, i64, i64, i32], ctypes.c_int64),
         "mlp_tp_shard_bwd": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -175,6 +178,23 @@ def mlp_tp_shard_fwd(X, W1r, b1r, W2r, H, Z, P, N, D, F, T, dtype, act, stream=N
                                  _ptr(H, dtype, "H"), _ptr(Z, dtype, "Z"), _ptr(P, F32, "P"),
                                  N, D, F, T, dtype, _act(act), _stream(stream))
     return _check(rc, "mlp_tp_shard_fwd")
+
+
+def mlp_tp_shard_fwd_workspace_bytes(N, D, F, T) -> int:
+    n = load().mlp_tp_shard_fwd_workspace_bytes(N, D, F, T)
+    if n < 0:
+        raise MlpTpError(int(n), "mlp_tp_shard_fwd_workspace_bytes")
+    return int(n)
+
+
+def mlp_tp_shard_fwd_ws(X, W1r, b1r, W2r, H, Z, P, workspace, workspace_bytes, N, D, F, T, dtype,
+                        act, stream=None):
+    rc = load().mlp_tp_shard_fwd_ws(_ptr(X, dtype, "X"), _ptr(W1r, dtype, "W1r"),
+                                    _ptr(b1r, dtype, "b1r"), _ptr(W2r, dtype, "W2r"),
+                                    _ptr(H, dtype, "H"), _ptr(Z, dtype, "Z"), _ptr(P, F32, "P"),
+                                    _ptr(workspace, None, "workspace"), int(workspace_bytes),
+                                    N, D, F, T, dtype, _act(act), _stream(stream))
+    return _check(rc, "mlp_tp_shard_fwd_ws")
 
 
 def mlp_tp_partial_reduce(P, T, b2, b2_dtype, Y, N, D, stream=None):

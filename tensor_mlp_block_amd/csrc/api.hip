@@ -229,6 +229,48 @@ int mlp_tp_shard_fwd(const void* X, const void* W1r, const void* b1r, const void
     return launch_status();
 }
 
+int64_t mlp_tp_shard_fwd_workspace_bytes(int64_t N, int64_t D, int64_t F, int32_t T)
+{
+    if (int rc = check_shard_shape(N, D, F, T)) return rc;
+    if (N == 0) return 0;
+    return mlptp::fwd_split_workspace_bytes(N, D, F / T, MLP_TP_BF16);
+}
+
+int mlp_tp_shard_fwd_ws(const void* X, const void* W1r, const void* b1r, const void* W2r, void* H,
+                        void* Z, float* P, void* workspace, size_t workspace_bytes, int64_t N,
+                        int64_t D, int64_t F, int32_t T, int32_t dtype, int32_t act, void* stream)
+{
+    if (int rc = check_up(X, W1r, b1r, Z, H, N, D, F, T, dtype, act)) return rc;
+    if (int rc = check_down(H, W2r, P, N, D, F, T, dtype)) return rc;
+    if (workspace && !aligned16(workspace)) return MLP_TP_E_ALIGN;
+    const int64_t wsb = workspace ? (int64_t)workspace_bytes : 0;
+    if (wsb < 0) return MLP_TP_E_WORKSPACE;
+    {
+        const int64_t es = elem_size(dtype), Fs = F / T;
+        if (int rc = disjoint({{P, N * D * 4}}, {{X, N * D * es}, {W1r, D * Fs * es},
+                                                  {b1r, Fs * es}, {Z, N * Fs * es}}))
+            return rc;
+        if (int rc = disjoint({{H, N * Fs * es}, {Z, N * Fs * es}}, {{W2r, Fs * D * es}}))
+            return rc;
+        if (int rc = disjoint({{workspace, wsb}},
+                              {{X, N * D * es}, {W1r, D * Fs * es}, {b1r, Fs * es},
+                               {W2r, Fs * D * es}, {H, N * Fs * es}, {Z, N * Fs * es},
+                               {P, N * D * 4}}))
+            return rc;
+    }
+    if (N == 0) return MLP_TP_OK;
+    if (int rc = hip_clean()) return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // Both products split as planned, or neither: a workspace below the query's size (the
+    // larger product's planes) leaves the shard exactly mlp_tp_shard_fwd.
+    const int64_t need = mlptp::fwd_split_workspace_bytes(N, D, F / T, dtype);
+    float* ws = (need > 0 && wsb >= need) ? static_cast<float*>(workspace) : nullptr;
+    mlptp::launch_up_proj(X, W1r, b1r, Z, H, N, D, F / T, dtype, act, s, ws, wsb);
+    if (int rc = launch_status()) return rc;
+    mlptp::launch_down_proj(H, W2r, P, N, D, F / T, dtype, s, ws, wsb);
+    return launch_status();
+}
+
 int mlp_tp_partial_reduce(const float* const* P, int32_t T, const void* b2, int32_t b2_dtype,
                           float* Y, int64_t N, int64_t D, void* stream)
 {

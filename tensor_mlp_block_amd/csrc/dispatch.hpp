@@ -78,16 +78,18 @@ inline void run_mfma(const void* A, const void* B, int64_t M, int64_t N, int64_t
 
 // N counts output columns; a dual epilogue takes two B operands (B2 non-null) whose tiles
 // share the workgroup's B region, so each tile covers BN / 2 output columns.
+// `splits` > 1 cuts the contraction into ranges of kc (a multiple of 64), one grid row each.
 template <class Cfg, bool A_KC, bool B_KC, class Epi>
 inline void run_dma(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int64_t lda,
-                    int64_t ldb, Epi epi, hipStream_t s, const void* B2 = nullptr)
+                    int64_t ldb, Epi epi, hipStream_t s, const void* B2 = nullptr,
+                    int splits = 1, int64_t kc = 0)
 {
     constexpr int BNO = EpiIsDual<Epi>::value ? Cfg::BN / 2 : Cfg::BN;
     const int64_t tiles = ceil_div(M, Cfg::BM) * ceil_div(N, BNO);
-    hipLaunchKernelGGL((gemm_bf16_dma<Cfg, A_KC, B_KC, Epi>), dim3((uint32_t)tiles),
+    hipLaunchKernelGGL((gemm_bf16_dma<Cfg, A_KC, B_KC, Epi>), dim3((uint32_t)tiles, splits),
                        dim3(Cfg::NTHREADS), 0, s, static_cast<const uint16_t*>(A),
                        static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2), M, N,
-                       K, lda, ldb, epi);
+                       K, lda, ldb, epi, splits > 1 ? kc : K);
 }
 
 // The tile a bf16 product of M x N outputs (contraction K, leading dimensions lda, ldb) runs
@@ -124,6 +126,53 @@ inline void run_bf16(const void* A, const void* B, int64_t M, int64_t N, int64_t
     case kTileRegStaged: run_mfma<DefaultTile, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
     default: run_dma<DmaTile256x256, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s); break;
     }
+}
+
+// A split of the contraction for products with fewer 128 x 128 tiles than compute units: each
+// split's workgroups write an fp32 partial plane of the whole [M, N] product into a caller-owned
+// workspace, and a second, streaming pass sums the planes in split order and applies the
+// product's epilogue. Deterministic (no atomics); only the order of the fp32 additions differs
+// from the unsplit product. S = min(8, 2 CUs / tiles, K / 1024): at most two workgroups per CU,
+// and each split at least 1024 deep (sixteen 64-deep stages), so the extra launch and the planes'
+// traffic stay small beside the GEMM. Measured (one MI355X, GEMM plus the sum of the planes, us):
+// the pages' example shape's products (256 tokens) 57 -> 46 (up, T = 1, S = 2), 134 -> 42
+// (down, T = 1, S = 8), 53 -> 33 (up, T = 2, S = 4), 53 -> 24 (up, T = 8, S = 4); a 1024-token
+// Llama-width up-projection (224 tiles) 101 -> 72 (S = 2). Products with as many tiles as CUs
+// lost (GPT-2-medium's down-projection, 256 tiles: 29 -> 32 at S = 2), and so did splits below
+// 1024 (T = 8 down-projection, K = 1376: 17.1 -> 18.4 at S = 2).
+struct SplitPlan {
+    int splits;
+    int64_t kc;  // contraction length per split (a multiple of 64)
+};
+
+inline SplitPlan split_plan(bool a_kc, bool b_kc, int64_t M, int64_t N, int64_t K, int64_t lda,
+                            int64_t ldb, int64_t cus)
+{
+    const SplitPlan none{1, K};
+    if (choose_tile(a_kc, b_kc, M, N, K, lda, ldb, cus) != kTile128x128) return none;
+    const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 128);
+    if (tiles >= cus) return none;
+    int64_t S = 2 * cus / tiles;
+    if (S > 8) S = 8;
+    if (S > K / 1024) S = K / 1024;
+    if (S < 2) return none;
+    const int64_t kc = ceil_div(ceil_div(K, S), 64) * 64;
+    return SplitPlan{(int)ceil_div(K, kc), kc};
+}
+
+// Workspace bytes of a split product: one fp32 [M, N] plane per split.
+inline int64_t split_workspace_bytes(const SplitPlan& p, int64_t M, int64_t N)
+{
+    return p.splits > 1 ? (int64_t)p.splits * M * N * 4 : 0;
+}
+
+// The split GEMM: fp32 planes ws[s][M, N] on the 128 x 128 tile.
+template <bool A_KC, bool B_KC>
+inline void run_split(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int64_t lda,
+                      int64_t ldb, const SplitPlan& p, float* ws, hipStream_t s)
+{
+    EpiSplitF32 epi{ws, M * N, N, (int)(N % 4 == 0)};
+    run_dma<DmaTile128x128, A_KC, B_KC>(A, B, M, N, K, lda, ldb, epi, s, nullptr, p.splits, p.kc);
 }
 
 template <bool A_KC, bool B_KC, class Epi>

@@ -65,9 +65,12 @@ __device__ __forceinline__ void store1<float>(float* p, float v) { *p = v; }
 // bias column of the first vector is one 64-bit remainder per thread; the next vectors' columns
 // are 4 kEwBlock elements further on, so each follows by one add and at most one subtraction
 // (`step` = 4 kEwBlock mod Fs, from the host).
+// Z holds S planes `plane` elements apart (S > 1: the fp32 partials of a split contraction),
+// summed in plane order before the bias; Zout, when non-null, keeps the pre-activation.
 template <class T, int ACT>
-__global__ __launch_bounds__(kEwBlock) void bias_act_vec(const float* __restrict__ Z,
-                                                         const T* __restrict__ b,
+__global__ __launch_bounds__(kEwBlock) void bias_act_vec(const float* __restrict__ Z, int S,
+                                                         int64_t plane, const T* __restrict__ b,
+                                                         T* __restrict__ Zout,
                                                          T* __restrict__ H, int64_t nvec,
                                                          int64_t Fs, int64_t v0, int64_t step)
 {
@@ -80,6 +83,14 @@ __global__ __launch_bounds__(kEwBlock) void bias_act_vec(const float* __restrict
         z[u] = v < nvec ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Z) + v)
                         : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    for (int p = 1; p < S; ++p) {
+        const f32x4* Zp = reinterpret_cast<const f32x4*>(Z + p * plane);
+#pragma unroll
+        for (int u = 0; u < kEwVecs; ++u) {
+            const int64_t v = base + u * kEwBlock;
+            if (v < nvec) z[u] += __builtin_nontemporal_load(Zp + v);
+        }
+    }
 #pragma unroll
     for (int u = 0; u < kEwVecs; ++u) {
         const int64_t v = base + u * kEwBlock;
@@ -90,6 +101,7 @@ __global__ __launch_bounds__(kEwBlock) void bias_act_vec(const float* __restrict
             col += step;
             if (col >= Fs) col -= Fs;
         }
+        if (Zout) store4_to<T>(Zout + v * 4, x);
         f32x4 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = act_fwd<ACT>(x[e]);
@@ -99,20 +111,24 @@ __global__ __launch_bounds__(kEwBlock) void bias_act_vec(const float* __restrict
 
 // Element path for Fs % 4 != 0.
 template <class T, int ACT>
-__global__ __launch_bounds__(256) void bias_act_scalar(const float* __restrict__ Z,
-                                                       const T* __restrict__ b,
-                                                       T* __restrict__ H, int64_t n, int64_t Fs)
+__global__ __launch_bounds__(256) void bias_act_scalar(const float* __restrict__ Z, int S,
+                                                       int64_t plane, const T* __restrict__ b,
+                                                       T* __restrict__ Zout, T* __restrict__ H,
+                                                       int64_t n, int64_t Fs)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
         float x = Z[e];
+        for (int p = 1; p < S; ++p) x += Z[p * plane + e];
         if (b) x += load1<T>(b, e % Fs);
+        if (Zout) store1<T>(Zout + e, x);
         store1<T>(H + e, act_fwd<ACT>(x));
     }
 }
 
 template <class T, int ACT>
-void launch_typed(const float* Z, const T* b, T* H, int64_t N, int64_t Fs, hipStream_t s)
+void launch_typed(const float* Z, int S, int64_t plane, const T* b, T* Zout, T* H, int64_t N,
+                  int64_t Fs, hipStream_t s)
 {
     const int64_t n = N * Fs;
     if (Fs % 4 == 0) {
@@ -122,14 +138,25 @@ void launch_typed(const float* Z, const T* b, T* H, int64_t N, int64_t Fs, hipSt
             const int64_t groups = ceil_div(nvec, per_group) - g0;
             hipLaunchKernelGGL((bias_act_vec<T, ACT>),
                                dim3((uint32_t)(groups < max_launch ? groups : max_launch)),
-                               dim3(kEwBlock), 0, s, Z, b, H, nvec, Fs, g0 * per_group,
-                               (int64_t)(4 * kEwBlock) % Fs);
+                               dim3(kEwBlock), 0, s, Z, S, plane, b, Zout, H, nvec, Fs,
+                               g0 * per_group, (int64_t)(4 * kEwBlock) % Fs);
         }
     } else {
         const int64_t groups = ceil_div(n, 256) < 4096 ? ceil_div(n, 256) : 4096;
         hipLaunchKernelGGL((bias_act_scalar<T, ACT>), dim3((uint32_t)groups), dim3(256), 0, s, Z,
-                           b, H, n, Fs);
+                           S, plane, b, Zout, H, n, Fs);
     }
+}
+
+template <class F>
+void with_dtype_act(int dtype, int act, F&& f)
+{
+    with_act(act, [&](auto a) {
+        if (dtype == kBF16)
+            f(a, uint16_t{});
+        else
+            f(a, float{});
+    });
 }
 
 }  // namespace
@@ -137,14 +164,17 @@ void launch_typed(const float* Z, const T* b, T* H, int64_t N, int64_t Fs, hipSt
 void launch_bias_act(const float* Z, const void* b1r, void* H, int64_t N, int64_t Fs, int dtype,
                      int act, hipStream_t s)
 {
-    with_act(act, [&](auto a) {
+    launch_split_bias_act(Z, 1, 0, b1r, nullptr, H, N, Fs, dtype, act, s);
+}
+
+void launch_split_bias_act(const float* planes, int S, int64_t plane, const void* b1r, void* Z,
+                           void* H, int64_t N, int64_t Fs, int dtype, int act, hipStream_t s)
+{
+    with_dtype_act(dtype, act, [&](auto a, auto t) {
         constexpr int ACT = decltype(a)::value;
-        if (dtype == kBF16)
-            launch_typed<uint16_t, ACT>(Z, static_cast<const uint16_t*>(b1r),
-                                        static_cast<uint16_t*>(H), N, Fs, s);
-        else
-            launch_typed<float, ACT>(Z, static_cast<const float*>(b1r), static_cast<float*>(H), N,
-                                     Fs, s);
+        using T = decltype(t);
+        launch_typed<T, ACT>(planes, S, plane, static_cast<const T*>(b1r), static_cast<T*>(Z),
+                             static_cast<T*>(H), N, Fs, s);
     });
 }
 

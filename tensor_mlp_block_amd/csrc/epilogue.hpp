@@ -202,6 +202,35 @@ struct EpiBiasShare {
     }
 };
 
+// One split of a split contraction: the fp32 partial of split blockIdx.y goes to its own plane
+// C + blockIdx.y * plane (ldc N) of a workspace, stored normally so that the pass summing the
+// planes, which follows at once, finds them in the caches.
+struct EpiSplitF32 {
+    float* C;
+    int64_t plane;
+    int64_t ldc;
+    int vec;
+    using ColData = NoData;
+    using ElemData = NoData;
+    static constexpr bool kColData = false, kElemData = false;
+    __device__ __forceinline__ ColData col_load(int64_t, int64_t) const { return {}; }
+    __device__ __forceinline__ ElemData elem_load(int64_t, int64_t, int64_t, int64_t) const
+    {
+        return {};
+    }
+    __device__ __forceinline__ void apply(int64_t row, int64_t col, f32x4 v, ColData, ElemData,
+                                          int64_t M, int64_t N) const
+    {
+        const int n = valid4(row, col, M, N);
+        if (n) store4(C + (int64_t)blockIdx.y * plane + row * ldc + col, v, n, vec);
+    }
+    __device__ __forceinline__ void operator()(int64_t row, int64_t col, f32x4 v, int64_t M,
+                                               int64_t N) const
+    {
+        apply(row, col, v, {}, {}, M, N);
+    }
+};
+
 // fp32 accumulation C += v: a down-projection adding its partial into one running buffer,
 // the sequential one-GPU form of the block-tail sum [Z 02]. Each element is read and written
 // by the same lane, so the update needs no atomics.

@@ -35,8 +35,19 @@ int compute_units()
 // GEMM view: M = N tokens, N = Fs, K = D; A = X (k-contiguous), B = W1r [D, Fs]
 // (n-contiguous, transposed into LDS).
 void launch_up_proj(const void* X, const void* W1r, const void* b1r, void* Z, void* H, int64_t N,
-                    int64_t D, int64_t Fs, int dtype, int act, hipStream_t s)
+                    int64_t D, int64_t Fs, int dtype, int act, hipStream_t s, float* ws,
+                    int64_t ws_bytes)
 {
+    if (ws && dtype == kBF16) {
+        const SplitPlan p = split_plan(true, false, N, Fs, D, D, Fs, compute_units());
+        if (p.splits > 1 && split_workspace_bytes(p, N, Fs) <= ws_bytes) {
+            // fp32 planes of X W1r over the contraction's ranges, then bias and phi over their
+            // sum: the same epilogue arithmetic as the fused form.
+            run_split<true, false>(X, W1r, N, Fs, D, D, Fs, p, ws, s);
+            launch_split_bias_act(ws, p.splits, N * Fs, b1r, Z, H, N, Fs, dtype, act, s);
+            return;
+        }
+    }
     const int vec = (Fs % 4 == 0);
     with_act(act, [&](auto a) {
         constexpr int ACT = decltype(a)::value;
@@ -57,13 +68,35 @@ void launch_up_proj(const void* X, const void* W1r, const void* b1r, void* Z, vo
 // GEMM view: M = N tokens, N = D, K = Fs; A = H (k-contiguous), B = W2r [Fs, D]
 // (n-contiguous).
 void launch_down_proj(const void* H, const void* W2r, float* P, int64_t N, int64_t D, int64_t Fs,
-                      int dtype, hipStream_t s)
+                      int dtype, hipStream_t s, float* ws, int64_t ws_bytes)
 {
+    if (ws && dtype == kBF16) {
+        const SplitPlan p = split_plan(true, false, N, D, Fs, Fs, D, compute_units());
+        if (p.splits > 1 && split_workspace_bytes(p, N, D) <= ws_bytes) {
+            // fp32 planes of H W2r over the contraction's ranges, summed in order into P.
+            run_split<true, false>(H, W2r, N, D, Fs, Fs, D, p, ws, s);
+            const float* planes[8];
+            for (int i = 0; i < p.splits; ++i) planes[i] = ws + (int64_t)i * N * D;
+            launch_partial_reduce(planes, p.splits, nullptr, kF32, P, N, D, s);
+            return;
+        }
+    }
     EpiStoreF32 epi{P, D, (int)(D % 4 == 0)};
     if (dtype == kBF16)
         run_bf16<true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
     else
         run_simt<true, false>(H, W2r, N, D, Fs, Fs, D, epi, s);
+}
+
+int64_t fwd_split_workspace_bytes(int64_t N, int64_t D, int64_t Fs, int dtype)
+{
+    if (dtype != kBF16 || N == 0) return 0;
+    const int64_t cus = compute_units();
+    const int64_t up =
+        split_workspace_bytes(split_plan(true, false, N, Fs, D, D, Fs, cus), N, Fs);
+    const int64_t down =
+        split_workspace_bytes(split_plan(true, false, N, D, Fs, Fs, D, cus), N, D);
+    return up > down ? up : down;
 }
 
 // P^(r) = H^(r) W2^(r) + b2 / T: each rank adds its 1/T share of b2 to its own partial, so the

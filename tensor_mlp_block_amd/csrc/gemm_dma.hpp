@@ -363,12 +363,22 @@ struct EpiIsDual<E, std::void_t<decltype(E::kDual)>> : std::bool_constant<E::kDu
 
 // C[M, N] = A B, or in the dual form the pair (A B, A B2) handed to epi.apply_dual: one A tile
 // in LDS feeds both products, as the gated MLP's gate and up projections need [Z 08].
+// With a grid of more than one row (gridDim.y = S), the contraction is split: workgroup
+// (x, s) sums k in [s kc, min(K, (s + 1) kc)) only (kc a multiple of 64) and its epilogue
+// tells the splits apart by blockIdx.y.
 template <class Cfg, bool A_KC, bool B_KC, class Epi>
 __global__ __launch_bounds__(Cfg::NTHREADS, Cfg::MIN_WAVES_PER_SIMD) void gemm_bf16_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const uint16_t* __restrict__ B2, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
-    Epi epi)
+    Epi epi, int64_t kc)
 {
+    if (gridDim.y > 1) {
+        const int64_t k0 = (int64_t)blockIdx.y * kc;
+        K = (K - k0) < kc ? (K - k0) : kc;
+        A += A_KC ? k0 : k0 * lda;
+        B += B_KC ? k0 : k0 * ldb;
+        if (B2) B2 += B_KC ? k0 : k0 * ldb;
+    }
     constexpr bool DUAL = EpiIsDual<Epi>::value;
     constexpr int BNO = DUAL ? Cfg::BN / 2 : Cfg::BN;    // output columns per tile
     constexpr int WTNO = DUAL ? Cfg::WTN / 2 : Cfg::WTN;  // output columns per wave

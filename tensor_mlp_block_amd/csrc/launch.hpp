@@ -14,12 +14,19 @@ constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 
 // Z = X W1r + b1r; H = phi(Z). X [N, D], W1r [D, Fs], b1r [Fs] or null, Z/H [N, Fs].
+// With a workspace `ws` of at least fwd_split_workspace_bytes bytes, a product with too few
+// tiles to fill the GPU splits its contraction (fp32 planes in ws, then a streaming pass).
 void launch_up_proj(const void* X, const void* W1r, const void* b1r, void* Z, void* H, int64_t N,
-                    int64_t D, int64_t Fs, int dtype, int act, hipStream_t s);
+                    int64_t D, int64_t Fs, int dtype, int act, hipStream_t s,
+                    float* ws = nullptr, int64_t ws_bytes = 0);
 
-// P = H W2r. H [N, Fs], W2r [Fs, D], P [N, D] fp32.
+// P = H W2r. H [N, Fs], W2r [Fs, D], P [N, D] fp32. Workspace as for launch_up_proj.
 void launch_down_proj(const void* H, const void* W2r, float* P, int64_t N, int64_t D, int64_t Fs,
-                      int dtype, hipStream_t s);
+                      int dtype, hipStream_t s, float* ws = nullptr, int64_t ws_bytes = 0);
+
+// Workspace bytes the split forms of the forward's two products use on the current device (the
+// larger of the two, since they run one after the other); 0 when neither splits.
+int64_t fwd_split_workspace_bytes(int64_t N, int64_t D, int64_t Fs, int dtype);
 
 // P = H W2r + b2 / T: rank r's partial carrying its share of b2. b2 [D] of b2_dtype, nullable.
 void launch_down_proj_bias_share(const void* H, const void* W2r, const void* b2, int b2_dtype,
@@ -77,6 +84,11 @@ void launch_colsum(const void* dZ, float* ws, float* db1, int64_t N, int64_t Fs,
 // H = phi(Z + b1r): Z [N, Fs] fp32, b1r [Fs] (dtype, nullable), H [N, Fs] dtype.
 void launch_bias_act(const float* Z, const void* b1r, void* H, int64_t N, int64_t Fs, int dtype,
                      int act, hipStream_t s);
+
+// The same over the sum of S fp32 planes [N, Fs] `plane` elements apart (the partials of a split
+// contraction, summed in plane order), keeping the pre-activation in Z when non-null.
+void launch_split_bias_act(const float* planes, int S, int64_t plane, const void* b1r, void* Z,
+                           void* H, int64_t N, int64_t Fs, int dtype, int act, hipStream_t s);
 
 // Y = ((P[0] + P[1]) + ...) + b2 over T fp32 [N, D] partials (P is a host array).
 void launch_partial_reduce(const float* const* P, int T, const void* b2, int b2_dtype, float* Y,

@@ -79,14 +79,18 @@ static std::string fmt(const char* name, int64_t a, int64_t b, int64_t c)
 
 namespace mlptp {
 void launch_up_proj(const void*, const void*, const void*, void*, void*, int64_t N, int64_t D,
-                    int64_t Fs, int, int, hipStream_t)
+                    int64_t Fs, int, int, hipStream_t, float* ws, int64_t ws_bytes)
 {
-    record(fmt("up", N, D, Fs));
+    record(fmt("up", N, D, Fs) + (ws ? " ws" + std::to_string(ws_bytes) : ""));
 }
 void launch_down_proj(const void*, const void*, float*, int64_t N, int64_t D, int64_t Fs, int,
-                      hipStream_t)
+                      hipStream_t, float* ws, int64_t ws_bytes)
 {
-    record(fmt("down", N, D, Fs));
+    record(fmt("down", N, D, Fs) + (ws ? " ws" + std::to_string(ws_bytes) : ""));
+}
+int64_t fwd_split_workspace_bytes(int64_t N, int64_t D, int64_t Fs, int)
+{
+    return N * (D > Fs ? D : Fs) * 4;
 }
 void launch_down_proj_accumulate(const void*, const void*, float*, int64_t N, int64_t D,
                                  int64_t Fs, int, hipStream_t)
@@ -229,6 +233,32 @@ static void check_forward_calls()
     CHECK(mlp_tp_shard_fwd(addr(0x10000), addr(0x200000), nullptr, addr(0x400000),
                            addr(0x600000), nullptr, faddr(0x800000), 4, 8, 18, 4, MLP_TP_BF16,
                            MLP_TP_ACT_GELU_TANH, nullptr) == MLP_TP_E_INDIVISIBLE);
+    CHECK(g_calls.empty());
+    // the split-contraction forward: the caller's workspace reaches both products; without
+    // one it is exactly the plain forward
+    reset();
+    CHECK(mlp_tp_shard_fwd_workspace_bytes(4, 8, 16, 2) == 4 * 8 * 4);
+    CHECK(mlp_tp_shard_fwd_ws(addr(0x10000), addr(0x200000), nullptr, addr(0x400000),
+                              addr(0x600000), nullptr, faddr(0x800000), addr(0x900000), 128, 4, 8,
+                              16, 2, MLP_TP_BF16, MLP_TP_ACT_GELU_TANH, nullptr) == MLP_TP_OK);
+    CHECK(g_calls.size() == 2 && g_calls[0] == "up 4 8 8 ws128" &&
+          g_calls[1] == "down 4 8 8 ws128");
+    reset();
+    CHECK(mlp_tp_shard_fwd_ws(addr(0x10000), addr(0x200000), nullptr, addr(0x400000),
+                              addr(0x600000), nullptr, faddr(0x800000), nullptr, 0, 4, 8, 16, 2,
+                              MLP_TP_BF16, MLP_TP_ACT_GELU_TANH, nullptr) == MLP_TP_OK);
+    CHECK(g_calls.size() == 2 && g_calls[0] == "up 4 8 8" && g_calls[1] == "down 4 8 8");
+    // a workspace below the query's size: neither product gets it
+    reset();
+    CHECK(mlp_tp_shard_fwd_ws(addr(0x10000), addr(0x200000), nullptr, addr(0x400000),
+                              addr(0x600000), nullptr, faddr(0x800000), addr(0x900000), 127, 4, 8,
+                              16, 2, MLP_TP_BF16, MLP_TP_ACT_GELU_TANH, nullptr) == MLP_TP_OK);
+    CHECK(g_calls.size() == 2 && g_calls[0] == "up 4 8 8" && g_calls[1] == "down 4 8 8");
+    reset();
+    CHECK(mlp_tp_shard_fwd_ws(addr(0x10000), addr(0x200000), nullptr, addr(0x400000),
+                              addr(0x600000), nullptr, faddr(0x800000), addr(0x800010), 128, 4, 8,
+                              16, 2, MLP_TP_BF16, MLP_TP_ACT_GELU_TANH,
+                              nullptr) == MLP_TP_E_ALIAS);  // workspace over P
     CHECK(g_calls.empty());
     // b2 share: the rank count travels to the epilogue [Z 05]
     reset();

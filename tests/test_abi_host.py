@@ -390,3 +390,31 @@ def test_noalloc_backward_checks(lib):
                N=32776, D=64, F=4096, T=1)
     assert mt.mlp_tp_shard_bwd_workspace_bytes(32776, 64, 4096, 1) > mt.NOALLOC_SCRATCH_BYTES
     assert call(**big) == mt.E_WORKSPACE
+
+
+def test_split_forward_workspace_query_and_checks(lib):
+    """The split-contraction forward [Z 04]: the workspace query (this container has no GPU, so
+    the library sizes for 256 compute units) and the host checks of mlp_tp_shard_fwd_ws."""
+    # the pages' example shape at T = 1: the down-projection's 64 tiles of 128 x 128 split
+    # 8 ways (8 fp32 planes of [256, 4096]); the Llama shard fills the GPU and never splits
+    assert mt.mlp_tp_shard_fwd_workspace_bytes(256, 4096, 11008, 1) == 8 * 256 * 4096 * 4
+    assert mt.mlp_tp_shard_fwd_workspace_bytes(4096, 8192, 28672, 8) == 0
+    assert mt.mlp_tp_shard_fwd_workspace_bytes(0, 4096, 11008, 1) == 0
+    assert lib.mlp_tp_shard_fwd_workspace_bytes(4, 8, 18, 4) == mt.E_INDIVISIBLE
+    f = lib.mlp_tp_shard_fwd_ws
+
+    def call(**kw):
+        a = dict(X=A, W1r=B, b1r=None, W2r=C, H=Dp, Z=None, P=E, ws=G, wsb=1 << 20, N=4, D=8,
+                 F=16, T=2, dtype=mt.BF16, act=mt.ACT["gelu_tanh"])
+        a.update(kw)
+        return f(a["X"], a["W1r"], a["b1r"], a["W2r"], a["H"], a["Z"], a["P"], a["ws"],
+                 a["wsb"], a["N"], a["D"], a["F"], a["T"], a["dtype"], a["act"], S)
+
+    assert call(X=None) == mt.E_NULL
+    assert call(F=18, T=4) == mt.E_INDIVISIBLE
+    assert call(ws=G + 8) == mt.E_ALIGN
+    assert call(ws=E) == mt.E_ALIAS          # workspace over P
+    assert call(ws=A + 16) == mt.E_ALIAS     # workspace over X
+    assert call(H=A) == mt.E_ALIAS
+    assert call(N=0) == mt.OK
+    assert call(N=0, ws=None, wsb=0) == mt.OK

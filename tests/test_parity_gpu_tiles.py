@@ -8,6 +8,8 @@ the b2/T form of the block tail.
   weight, summed with b2 once, on sampled token rows [Z 11].
 * b2 split over the ranks [Z 05]: bit-exact on integer data for T a power of two, within
   rounding otherwise, and on the bf16 shapes.
+* The split-contraction forward (mlp_tp_shard_fwd_ws) on shapes with too few tiles to fill the
+  GPU [Z 04], element by element, deterministic, and unsplit when the workspace is short.
 
 Bars as in test_parity_gpu.py: bit-exact on integer-valued fp32 data, else
 max|gpu - ref| / max|ref| <= 1e-2 per output tensor.
@@ -24,6 +26,7 @@ import torch
 import oracle
 from tensor_mlp_block_amd import binding as mt
 from tensor_mlp_block_amd import synth, workloads
+from tensor_mlp_block_amd.workloads import Workload
 from tile_cases import EDGE_CASES
 
 pytestmark = pytest.mark.gpu
@@ -245,3 +248,59 @@ def test_bias_share_at_three_ranks():
     once = oracle.block_fwd(Xc, synth.gen_W1(w), synth.gen_b1(w), synth.gen_W2(w), b2, 3,
                             act=w.act)
     assert_close("Y against b2 once", Y, once, 1e-6)
+
+
+# --------------------------------------------------------------------------------------------
+# Split contractions for products with too few tiles to fill the GPU [Z 04]
+# --------------------------------------------------------------------------------------------
+
+SPLIT_CASES = [
+    # the pages' example shape (d_model 4096, d_ff 11008, 2 x 128 tokens) for each T
+    workloads.PAGE_EXAMPLE_MLP.with_(T=1),
+    workloads.PAGE_EXAMPLE_MLP.with_(T=8),
+    # ragged everywhere: 200 tokens, D = 1000, Fs = 3000 (splits of the 3000- and 1000-deep
+    # contractions end mid-stage)
+    Workload("split_ragged_n200_d1000_f6000_t2", 200, 1000, 6000, 2, "gelu_erf", "bf16", 7301,
+             "normal"),
+]
+
+
+@pytest.mark.parametrize("w", SPLIT_CASES, ids=lambda w: w.name)
+def test_split_contraction_forward_matches_oracle(w):
+    """mlp_tp_shard_fwd_ws with the workspace its query asks for: Z, H and P element by element
+    against the oracle; the unsplit call agrees within the same bar; two calls agree bit for bit
+    (the partials are summed in a fixed order); a workspace one byte short leaves the products
+    unsplit, bit for bit mlp_tp_shard_fwd."""
+    _say(f"  workload {w.name}")
+    nb = mt.mlp_tp_shard_fwd_workspace_bytes(w.N, w.D, w.F, w.T)
+    _say(f"    workspace {nb} bytes")
+    assert nb > 0, "these shapes are meant to split on a 256-CU GPU"
+    Xc = synth.gen_X(w)
+    W1c, b1c, W2c = (synth.gen_W1(w, 0, w.Fs), synth.gen_b1(w, 0, w.Fs),
+                     synth.gen_W2(w, 0, w.Fs))
+    X, W1, b1, W2 = (t.cuda() for t in (Xc, W1c, b1c, W2c))
+    ws = torch.empty((nb,), dtype=torch.uint8, device="cuda")
+
+    def run(wsp, wsb):
+        H = torch.empty((w.N, w.Fs), dtype=torch.bfloat16, device="cuda")
+        Z = torch.empty_like(H)
+        P = torch.empty((w.N, w.D), device="cuda")
+        if wsp is None:
+            mt.mlp_tp_shard_fwd(X, W1, b1, W2, H, Z, P, w.N, w.D, w.F, w.T, mt.BF16, w.act)
+        else:
+            mt.mlp_tp_shard_fwd_ws(X, W1, b1, W2, H, Z, P, wsp, wsb, w.N, w.D, w.F, w.T, mt.BF16,
+                                   w.act)
+        torch.cuda.synchronize()
+        return Z, H, P
+
+    Zs, Hs, Ps = run(ws, nb)
+    Zr, Hr, Pr = oracle.shard_fwd(Xc, W1c, b1c, W2c, 1, 0, act=w.act)
+    assert_close("Z (split)", Zs, Zr)
+    assert_close("H (split)", Hs, Hr)
+    assert_close("P (split)", Ps, Pr)
+    Zu, Hu, Pu = run(None, 0)
+    assert_close("P (unsplit)", Pu, Pr)
+    again = run(ws, nb)
+    assert all(torch.equal(a, b) for a, b in zip(again, (Zs, Hs, Ps))), "split not deterministic"
+    short = run(ws, nb - 1)
+    assert all(torch.equal(a, b) for a, b in zip(short, (Zu, Hu, Pu))), "short workspace split"
