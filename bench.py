@@ -70,6 +70,31 @@ def read_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def read_profiled(kernel: str, workload: str, flop: float, sclk_live):
+    """The committed kernel trace of the headline command (rocprofv3 --kernel-trace): the
+    profiled run whose reported shader clock is nearest this run's, its rocprof mean duration
+    of `kernel` over the timed steps, the fraction of peak that gives, and that fraction scaled
+    by this run's clock over the profiled run's (throughput follows the clock the box runs at).
+    `stale` is true when the kernel sources changed since the trace was taken."""
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    runs = [r for r in rec.get("runs", []) if kernel in r.get("kernels", {})]
+    if not runs:
+        return None
+    best = min(runs, key=lambda r: abs((r.get("sclk_mhz") or 0) - (sclk_live or 0)))
+    us = best["kernels"][kernel]["timed_avg_us"]
+    frac = flop / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS
+    out = {"source": f"profiles/kernel_trace_{workload}.txt", "runs": len(runs),
+           "stale": rec.get("source_hash") != kernel_source_hash(),
+           "rocprof_timed_avg_us": us, "frac": round(frac, 4), "sclk_mhz": best.get("sclk_mhz")}
+    if sclk_live and best.get("sclk_mhz"):
+        out["frac_scaled_to_this_sclk"] = round(frac * sclk_live / best["sclk_mhz"], 4)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,6 +217,8 @@ def main() -> int:
                          "mean_launch_ms": round(min(mean_up, mean_down), 5),
                          "achieved": round(gemm_flop / (min(mean_up, mean_down) * 1e-3) / 1e12, 2)},
     }
+
+    roofline["profiled"] = read_profiled(kernel_name, w.name, gemm_flop, sclk_mhz)
 
     rows = None
     if not args.no_rows:
