@@ -52,16 +52,22 @@ __device__ __forceinline__ f32x4 bias4(const void* b2, int b2_dtype, int64_t c)
 }
 
 // Vector path: D % 4 == 0, so the 4 elements of a vector share one row of b2's index space.
-// Each thread owns kVecs vectors spaced kBlock apart (so every load instruction of a wave is
-// one contiguous 1 KB run) and issues all T x kVecs loads before the first add: enough bytes
-// in flight per CU to cover HBM latency without a grid-stride loop.
-constexpr int kBlock = 256, kVecs = 4;
+// Each thread owns VECS vectors spaced kBlock apart (so every load instruction of a wave is
+// one contiguous 1 KB run) and issues all T x VECS loads before the first add: enough bytes
+// in flight per CU to cover HBM latency without a grid-stride loop. Four vectors per thread
+// where that still gives at least kMinGroups4 workgroups, two below (more workgroups for a
+// short sum). Measured at T = 8 (one MI355X, bit-identical): a 256-row slice of a
+// [2048, 12288] tail 23.4 -> 18.0 us with two; the whole [2048, 12288] tail 142.3 us with four
+// against 146.1 with two, and a [4096, 8192] sum 184.1 against 194.8.
+constexpr int kBlock = 256;
+constexpr int64_t kMinGroups4 = 2048;
 
-template <int TT>
+template <int TT, int VECS>
 __global__ __launch_bounds__(kBlock) void partial_reduce_vec(PartialPtrs P, int T, const void* b2,
                                                              int b2_dtype, float* Y, int64_t nvec,
                                                              int64_t D, int64_t v0)
 {
+    constexpr int kVecs = VECS;
     const int nt = TT > 0 ? TT : T;
     const int64_t base = v0 + (int64_t)blockIdx.x * (kBlock * kVecs) + threadIdx.x;
     f32x4 s[kVecs];
@@ -126,19 +132,31 @@ void launch_partial_reduce(const float* const* P, int T, const void* b2, int b2_
     if (D % 4 == 0) {
         // One launch per chunk of at most 2^30 workgroups (2^40 elements), so the grid size
         // always fits; a single launch covers anything that fits in one GPU's memory.
-        const int64_t nvec = n / 4, per_group = (int64_t)kBlock * kVecs;
+        const int64_t nvec = n / 4;
+        const int vecs = ceil_div(nvec, (int64_t)kBlock * 4) >= kMinGroups4 ? 4 : 2;
+        const int64_t per_group = (int64_t)kBlock * vecs;
         const int64_t max_launch = int64_t(1) << 30;
         for (int64_t g0 = 0; g0 < ceil_div(nvec, per_group); g0 += max_launch) {
             const int64_t groups = ceil_div(nvec, per_group) - g0;
             const dim3 grid((uint32_t)(groups < max_launch ? groups : max_launch)), block(kBlock);
             const int64_t v0 = g0 * per_group;
-            switch (T) {
-            case 1: hipLaunchKernelGGL(partial_reduce_vec<1>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D, v0); break;
-            case 2: hipLaunchKernelGGL(partial_reduce_vec<2>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D, v0); break;
-            case 4: hipLaunchKernelGGL(partial_reduce_vec<4>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D, v0); break;
-            case 8: hipLaunchKernelGGL(partial_reduce_vec<8>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D, v0); break;
-            default: hipLaunchKernelGGL(partial_reduce_vec<0>, grid, block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D, v0); break;
-            }
+            auto launch = [&](auto tt, auto vv) {
+                hipLaunchKernelGGL((partial_reduce_vec<decltype(tt)::value, decltype(vv)::value>), grid,
+                                   block, 0, s, pp, T, b2, b2_dtype, Y, nvec, D, v0);
+            };
+            auto with_t = [&](auto vv) {
+                switch (T) {
+                case 1: launch(std::integral_constant<int, 1>{}, vv); break;
+                case 2: launch(std::integral_constant<int, 2>{}, vv); break;
+                case 4: launch(std::integral_constant<int, 4>{}, vv); break;
+                case 8: launch(std::integral_constant<int, 8>{}, vv); break;
+                default: launch(std::integral_constant<int, 0>{}, vv); break;
+                }
+            };
+            if (vecs == 4)
+                with_t(std::integral_constant<int, 4>{});
+            else
+                with_t(std::integral_constant<int, 2>{});
         }
     } else {
         const int64_t groups = ceil_div(n, 256) < max_groups ? ceil_div(n, 256) : max_groups;
